@@ -1,0 +1,158 @@
+"""Seeded synthetic inputs, shared bit for bit by the HIP path and the oracle.
+
+This module only draws random numbers and rounds them once to the storage
+type (bf16, fp16 or fp32). It holds none of the arithmetic of the fused
+linear layer or the LayerNorm+GELU row kernel, so the oracle and the HIP path
+can both consume its arrays without sharing any method code.
+
+Every tensor gets its own numpy PCG64 stream ``default_rng([seed, config_id,
+tensor_id])``. Distributions follow the workload descriptions: ``N(0, 1/K)``
+for weights is read as a *variance* of 1/K (fan-in scaling); decimal spreads
+such as 0.02 and 0.1 are read as *standard deviations*.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Storage type codes (the same integers as the C header's dtype enum).
+F32, BF16, F16, F8E4M3 = 0, 1, 2, 3
+
+_NP_STORE = {F32: np.float32, BF16: np.uint16, F16: np.float16, F8E4M3: np.uint8}
+
+
+def rng_for(config_id: int, tensor_id: int, seed: int = 0) -> np.random.Generator:
+    """One independent PCG64 stream per (config, tensor)."""
+    return np.random.default_rng([seed, config_id, tensor_id])
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); returns uint16 bits.
+
+    Inputs are finite random draws, so NaN handling is not needed here.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def store(a32: np.ndarray, dtype: int) -> np.ndarray:
+    """Round a float32 array once to its storage type (bit pattern array for bf16)."""
+    if dtype == F32:
+        return np.ascontiguousarray(a32, dtype=np.float32)
+    if dtype == BF16:
+        return f32_to_bf16_bits(a32)
+    if dtype == F16:
+        return np.ascontiguousarray(a32, dtype=np.float32).astype(np.float16)
+    raise ValueError(f"unsupported storage dtype {dtype}")
+
+
+def to_f64(stored: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact stored values as float64 (bf16 patterns decoded)."""
+    if dtype == BF16:
+        return bf16_bits_to_f32(stored).astype(np.float64)
+    return np.asarray(stored).astype(np.float64)
+
+
+def normal(rng: np.random.Generator, shape, mean: float = 0.0, std: float = 1.0) -> np.ndarray:
+    z = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        z *= np.float32(std)
+    if mean != 0.0:
+        z += np.float32(mean)
+    return z
+
+
+# ---------------------------------------------------------------------------
+# Workloads. Each entry lists shapes, storage types and the distribution recipe;
+# ``make_inputs`` draws them. ``config_id`` keys the random streams.
+# ---------------------------------------------------------------------------
+
+WORKLOADS = {
+    # Linear + bias + GELU(erf), fp32 in/out.
+    "linear_gelu_f32_64x256x256": dict(config_id=1, kind="linear", M=64, N=256, K=256,
+                                       in_dtype=F32, bias=True, act="gelu_erf", out_dtype=F32),
+    # LayerNorm + GELU(tanh) rows, fp16 in/out, fp32 statistics.
+    "ln_gelu_f16_32768x4096": dict(config_id=2, kind="ln", rows=32768, cols=4096,
+                                   io_dtype=F16, eps=1e-5, form="tanh"),
+    "ln_gelu_f16_32768x3000": dict(config_id=3, kind="ln", rows=32768, cols=3000,
+                                   io_dtype=F16, eps=1e-5, form="tanh"),
+    # Fused QKV projection + bias, split into three 4096x4096 outputs.
+    "qkv_bias_split_bf16_4096x12288x4096": dict(config_id=4, kind="linear", M=4096, N=12288, K=4096,
+                                                in_dtype=BF16, bias=True, act=None, split=3,
+                                                out_dtype=BF16),
+    # MLP-up + bias + GELU(erf).
+    "mlp_up_gelu_bf16_8192x16384x4096": dict(config_id=5, kind="linear", M=8192, N=16384, K=4096,
+                                             in_dtype=BF16, bias=True, act="gelu_erf",
+                                             out_dtype=BF16),
+    # Out-projection + residual + store residual stream + sum-sq partials + gamma; then finalize.
+    "outproj_residual_rms_bf16_16384x2048x2048": dict(config_id=6, kind="linear", M=16384, N=2048,
+                                                      K=2048, in_dtype=BF16, bias=False, act=None,
+                                                      residual=True, store_aux=True, rowsumsq=True,
+                                                      col_scale=True, out_dtype=BF16, eps=1e-6),
+    # Gate/up (pair-interleaved rows) + SwiGLU.
+    "gateup_swiglu_bf16_16384x16384x2048": dict(config_id=7, kind="linear", M=16384, N=16384, K=2048,
+                                                in_dtype=BF16, bias=False, act="swiglu",
+                                                out_dtype=BF16),
+    # Decode-shaped gate/up + SwiGLU + per-row FP8 e4m3 quantised writeback.
+    "decode_swiglu_fp8_bf16_32x16384x2048": dict(config_id=8, kind="linear", M=32, N=16384, K=2048,
+                                                 in_dtype=BF16, bias=False, act="swiglu",
+                                                 quant_fp8=True, out_dtype=F8E4M3),
+    # Same epilogue at prefill size.
+    "prefill_swiglu_fp8_bf16_16384x16384x2048": dict(config_id=9, kind="linear", M=16384, N=16384,
+                                                     K=2048, in_dtype=BF16, bias=False, act="swiglu",
+                                                     quant_fp8=True, out_dtype=F8E4M3),
+}
+
+# tensor ids inside one config
+_T_X, _T_W, _T_B, _T_Z, _T_GAMMA, _T_BETA = 0, 1, 2, 3, 4, 5
+
+
+def make_linear_inputs(spec: dict, seed: int = 0, M: int | None = None, N: int | None = None,
+                       K: int | None = None) -> dict:
+    """Draw X (M,K), W (N,K), optional b (N), z (M,N), gamma (N) for a linear workload.
+
+    Shapes may be overridden to get reduced cases with the same recipe.
+    X ~ N(0,1); W ~ N(0, var 1/K); b ~ N(0, std 0.02); z ~ N(0,1); gamma = 1 + N(0, std 0.1).
+    """
+    cid = spec["config_id"]
+    M = spec["M"] if M is None else M
+    N = spec["N"] if N is None else N
+    K = spec["K"] if K is None else K
+    dt = spec["in_dtype"]
+    out = {"M": M, "N": N, "K": K, "in_dtype": dt}
+    out["X"] = store(normal(rng_for(cid, _T_X, seed), (M, K)), dt)
+    out["W"] = store(normal(rng_for(cid, _T_W, seed), (N, K), std=float(1.0 / np.sqrt(K))), dt)
+    if spec.get("bias"):
+        out["b"] = store(normal(rng_for(cid, _T_B, seed), (N,), std=0.02), dt)
+    if spec.get("residual"):
+        out["z"] = store(normal(rng_for(cid, _T_Z, seed), (M, N)), BF16 if dt == BF16 else dt)
+    if spec.get("col_scale"):
+        out["gamma"] = store(normal(rng_for(cid, _T_GAMMA, seed), (N,), mean=1.0, std=0.1),
+                             BF16 if dt == BF16 else dt)
+    return out
+
+
+def make_ln_inputs(spec: dict, seed: int = 0, rows: int | None = None, cols: int | None = None) -> dict:
+    """Draw x (rows, cols) ~ N(0,1), gamma = 1 + N(0, std 0.1), beta ~ N(0, std 0.1), all fp16."""
+    cid = spec["config_id"]
+    rows = spec["rows"] if rows is None else rows
+    cols = spec["cols"] if cols is None else cols
+    dt = spec["io_dtype"]
+    return {
+        "rows": rows, "cols": cols, "io_dtype": dt,
+        "x": store(normal(rng_for(cid, _T_X, seed), (rows, cols)), dt),
+        "gamma": store(normal(rng_for(cid, _T_GAMMA, seed), (cols,), mean=1.0, std=0.1), dt),
+        "beta": store(normal(rng_for(cid, _T_BETA, seed), (cols,), std=0.1), dt),
+    }
+
+
+def random_stored(rng: np.random.Generator, shape, dtype: int, mean=0.0, std=1.0) -> np.ndarray:
+    """Free-form helper for tests: normal draws rounded to a storage type."""
+    return store(normal(rng, shape, mean=mean, std=std), dtype)
