@@ -1,0 +1,371 @@
+// C ABI of libfusedops.so (see include/fusedops.h): argument validation, op-list
+// canonicalisation, kernel selection and launch on the caller's stream.
+//
+// Every check runs on the host before anything is enqueued, so a validation error
+// leaves the stream untouched. No exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/fusedops.h"
+#include "epilogue.h"
+#include "kernels.h"
+
+using namespace fusedops;
+
+namespace {
+
+int dtype_size(int32_t dt) {
+  switch (dt) {
+    case FUSEDOPS_F32: return 4;
+    case FUSEDOPS_BF16: return 2;
+    case FUSEDOPS_F16: return 2;
+    case FUSEDOPS_F8E4M3: return 1;
+    default: return 0;
+  }
+}
+
+bool valid_dtype(int32_t dt) { return dt >= FUSEDOPS_F32 && dt <= FUSEDOPS_F8E4M3; }
+bool float_dtype(int32_t dt) { return dt == FUSEDOPS_F32 || dt == FUSEDOPS_BF16 || dt == FUSEDOPS_F16; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte extent of a row-major rows x cols tensor with leading dimension ld.
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  bool valid = false;
+};
+Span span2d(const void* p, int64_t rows, int64_t cols, int64_t ld, int es) {
+  Span s;
+  if (!p || rows <= 0 || cols <= 0) return s;
+  s.lo = reinterpret_cast<uintptr_t>(p);
+  s.hi = s.lo + (uintptr_t)(((rows - 1) * ld + cols) * es);
+  s.valid = true;
+  return s;
+}
+bool overlap(const Span& a, const Span& b) { return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Parsed epilogue op list.
+struct OpList {
+  const fusedops_op* by_kind[11] = {};
+  int act = ACT_NONE;
+  bool quant = false;
+};
+
+int32_t parse_ops(const fusedops_op* ops, int32_t n_ops, OpList& out) {
+  if (n_ops < 0 || (n_ops > 0 && !ops)) return FUSEDOPS_ERR_INVALID_ARG;
+  int last = 0;
+  int n_act = 0;
+  for (int i = 0; i < n_ops; ++i) {
+    const fusedops_op& op = ops[i];
+    if (op.kind < FUSEDOPS_OP_RESIDUAL_ADD || op.kind > FUSEDOPS_OP_SPLIT_COLS) return FUSEDOPS_ERR_INVALID_ARG;
+    if (op.kind <= last) return FUSEDOPS_ERR_INVALID_ARG;  // canonical order, each kind once
+    if (op.reserved != 0) return FUSEDOPS_ERR_INVALID_ARG;
+    last = op.kind;
+    out.by_kind[op.kind] = &op;
+    if (op.kind == FUSEDOPS_OP_GELU_ERF || op.kind == FUSEDOPS_OP_GELU_TANH || op.kind == FUSEDOPS_OP_SWIGLU)
+      ++n_act;
+  }
+  if (n_act > 1) return FUSEDOPS_ERR_INVALID_ARG;
+  if (out.by_kind[FUSEDOPS_OP_GELU_ERF]) out.act = ACT_GELU_ERF;
+  if (out.by_kind[FUSEDOPS_OP_GELU_TANH]) out.act = ACT_GELU_TANH;
+  if (out.by_kind[FUSEDOPS_OP_SWIGLU]) out.act = ACT_SWIGLU;
+  out.quant = out.by_kind[FUSEDOPS_OP_QUANT_FP8_ROW] != nullptr;
+  return FUSEDOPS_OK;
+}
+
+// Row blocks reserved in the FP8 workspace: enough for the finest token tile (32).
+int64_t ws_row_blocks(int64_t M) { return cdiv(M, 32); }
+size_t ws_bytes_for(int64_t M) {
+  const int64_t words = 2 + 2 * ws_row_blocks(M) + M;
+  return (size_t)(cdiv(words * 4, 256) * 256);
+}
+
+enum class Kernel { T256, SKINNY, F32 };
+
+// Map a launch result to a status; with FUSEDOPS_VERBOSE set, name the refused launch on stderr.
+int32_t launch_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return FUSEDOPS_OK;
+  const char* v = std::getenv("FUSEDOPS_VERBOSE");
+  if (v && *v && *v != '0') std::fprintf(stderr, "fusedops: launch of %s failed: %s (%d)\n", what, hipGetErrorName(err), (int)err);
+  return FUSEDOPS_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fusedops_abi_version(void) { return FUSEDOPS_ABI_VERSION; }
+int32_t fusedops_partial_cols(void) { return FUSEDOPS_PARTIAL_COLS; }
+
+const char* fusedops_status_string(int32_t status) {
+  switch (status) {
+    case FUSEDOPS_OK: return "ok";
+    case FUSEDOPS_ERR_INVALID_ARG: return "invalid argument";
+    case FUSEDOPS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FUSEDOPS_ERR_MISALIGNED: return "misaligned pointer, leading dimension or width";
+    case FUSEDOPS_ERR_WORKSPACE: return "workspace missing or too small";
+    case FUSEDOPS_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t fusedops_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, const fusedops_op* ops,
+                                       int32_t n_ops) {
+  (void)N;
+  (void)K;
+  OpList ol;
+  if (M < 1 || parse_ops(ops, n_ops, ol) != FUSEDOPS_OK) return 0;
+  return ol.quant ? ws_bytes_for(M) : 0;
+}
+
+int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int64_t ldw,
+                                 const void* bias, int64_t M, int64_t N, int64_t K,
+                                 int32_t in_dtype, const fusedops_op* ops, int32_t n_ops, void* Y,
+                                 int64_t ldy, int32_t out_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  // ---- scalars and enums
+  if (!X || !W) return FUSEDOPS_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1) return FUSEDOPS_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (in_dtype != FUSEDOPS_BF16 && in_dtype != FUSEDOPS_F32) return FUSEDOPS_ERR_UNSUPPORTED;
+  if (M > (1 << 30) || N > (1 << 30) || K > (1 << 30)) return FUSEDOPS_ERR_UNSUPPORTED;
+  OpList ol;
+  if (int32_t st = parse_ops(ops, n_ops, ol)) return st;
+  const fusedops_op* op_res = ol.by_kind[FUSEDOPS_OP_RESIDUAL_ADD];
+  const fusedops_op* op_aux = ol.by_kind[FUSEDOPS_OP_STORE_AUX];
+  const fusedops_op* op_par = ol.by_kind[FUSEDOPS_OP_ROWSUMSQ_PARTIAL];
+  const fusedops_op* op_gam = ol.by_kind[FUSEDOPS_OP_COL_SCALE];
+  const fusedops_op* op_row = ol.by_kind[FUSEDOPS_OP_ROW_SCALE];
+  const fusedops_op* op_q = ol.by_kind[FUSEDOPS_OP_QUANT_FP8_ROW];
+  const fusedops_op* op_split = ol.by_kind[FUSEDOPS_OP_SPLIT_COLS];
+  const bool swiglu = ol.act == ACT_SWIGLU;
+  const int64_t n_out = swiglu ? N / 2 : N;
+  const int64_t T = cdiv(N, FUSEDOPS_PARTIAL_COLS);
+  const int es_in = dtype_size(in_dtype);
+
+  // ---- output dtype rules
+  if (ol.quant) {
+    if (out_dtype != FUSEDOPS_F8E4M3) return FUSEDOPS_ERR_INVALID_ARG;
+  } else if (!float_dtype(out_dtype)) {
+    return FUSEDOPS_ERR_INVALID_ARG;
+  }
+  if (op_split) {
+    if (Y) return FUSEDOPS_ERR_INVALID_ARG;
+    if (swiglu || ol.quant) return FUSEDOPS_ERR_UNSUPPORTED;
+    if (op_split->n_split != 2 && op_split->n_split != 3) return FUSEDOPS_ERR_INVALID_ARG;
+    for (int i = 0; i < op_split->n_split; ++i)
+      if (!op_split->out_v[i]) return FUSEDOPS_ERR_INVALID_ARG;
+    if (N % op_split->n_split) return FUSEDOPS_ERR_INVALID_ARG;
+  } else if (!Y) {
+    return FUSEDOPS_ERR_INVALID_ARG;
+  }
+  const int es_out = dtype_size(out_dtype);
+
+  // ---- per-op fields
+  if (op_res && (!op_res->in || !float_dtype(op_res->dtype) || op_res->ld < N)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (op_aux && (!op_aux->out || !float_dtype(op_aux->dtype) || op_aux->ld < N)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (op_par && (!op_par->out || op_par->ld < T)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (op_gam && (!op_gam->in || !float_dtype(op_gam->dtype))) return FUSEDOPS_ERR_INVALID_ARG;
+  if (op_row && !op_row->in) return FUSEDOPS_ERR_INVALID_ARG;
+  if (op_q && !op_q->out) return FUSEDOPS_ERR_INVALID_ARG;
+  if (swiglu && (N % 2)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (ldx < K || ldw < K) return FUSEDOPS_ERR_INVALID_ARG;
+  if (Y && ldy < n_out) return FUSEDOPS_ERR_INVALID_ARG;
+  if (op_split && op_split->ld < N / op_split->n_split) return FUSEDOPS_ERR_INVALID_ARG;
+
+  // ---- alignment: 16-byte bases and rows; K and N granularity
+  const int k_gran = 16 / es_in;
+  if (K % k_gran || N % 8) return FUSEDOPS_ERR_MISALIGNED;
+  if (!aligned(X, 16) || !aligned(W, 16) || (ldx * es_in) % 16 || (ldw * es_in) % 16) return FUSEDOPS_ERR_MISALIGNED;
+  if (bias && !aligned(bias, 16)) return FUSEDOPS_ERR_MISALIGNED;
+  if (Y && (!aligned(Y, 16) || (ldy * es_out) % 16)) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_res && (!aligned(op_res->in, 16) || (op_res->ld * dtype_size(op_res->dtype)) % 16)) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_aux && (!aligned(op_aux->out, 16) || (op_aux->ld * dtype_size(op_aux->dtype)) % 16)) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_par && !aligned(op_par->out, 4)) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_gam && !aligned(op_gam->in, 16)) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_row && !aligned(op_row->in, 4)) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_q && !aligned(op_q->out, 4)) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_split) {
+    if ((N / op_split->n_split) % 8) return FUSEDOPS_ERR_MISALIGNED;
+    if ((op_split->ld * es_out) % 16) return FUSEDOPS_ERR_MISALIGNED;
+    for (int i = 0; i < op_split->n_split; ++i)
+      if (!aligned(op_split->out_v[i], 16)) return FUSEDOPS_ERR_MISALIGNED;
+  }
+
+  // ---- aliasing: outputs may not overlap inputs or each other, except Y == z exactly
+  Span in_spans[6] = {
+      span2d(X, M, K, ldx, es_in), span2d(W, N, K, ldw, es_in), span2d(bias, 1, N, N, es_in),
+      op_res ? span2d(op_res->in, M, N, op_res->ld, dtype_size(op_res->dtype)) : Span{},
+      op_gam ? span2d(op_gam->in, 1, N, N, dtype_size(op_gam->dtype)) : Span{},
+      op_row ? span2d(op_row->in, 1, M, M, 4) : Span{}};
+  Span out_spans[6];
+  int n_out_spans = 0;
+  if (Y) out_spans[n_out_spans++] = span2d(Y, M, n_out, ldy, es_out);
+  if (op_split)
+    for (int i = 0; i < op_split->n_split; ++i)
+      out_spans[n_out_spans++] = span2d(op_split->out_v[i], M, N / op_split->n_split, op_split->ld, es_out);
+  if (op_aux) out_spans[n_out_spans++] = span2d(op_aux->out, M, N, op_aux->ld, dtype_size(op_aux->dtype));
+  if (op_par) out_spans[n_out_spans++] = span2d(op_par->out, M, T, op_par->ld, 4);
+  if (op_q) out_spans[n_out_spans++] = span2d(op_q->out, 1, M, M, 4);
+  const bool y_is_z = Y && op_res && Y == op_res->in && ldy == op_res->ld && out_dtype == op_res->dtype &&
+                      !swiglu;
+  for (int o = 0; o < n_out_spans; ++o) {
+    for (int i = 0; i < 6; ++i) {
+      if (!overlap(out_spans[o], in_spans[i])) continue;
+      if (y_is_z && o == 0 && i == 3) continue;
+      return FUSEDOPS_ERR_INVALID_ARG;
+    }
+    for (int p = o + 1; p < n_out_spans; ++p)
+      if (overlap(out_spans[o], out_spans[p])) return FUSEDOPS_ERR_INVALID_ARG;
+  }
+
+  // ---- workspace
+  if (ol.quant) {
+    if (!workspace || workspace_bytes < ws_bytes_for(M) || !aligned(workspace, 4)) return FUSEDOPS_ERR_WORKSPACE;
+    const Span sw{reinterpret_cast<uintptr_t>(workspace),
+                  reinterpret_cast<uintptr_t>(workspace) + workspace_bytes, true};
+    for (int o = 0; o < n_out_spans; ++o)
+      if (overlap(sw, out_spans[o])) return FUSEDOPS_ERR_INVALID_ARG;
+    for (int i = 0; i < 6; ++i)
+      if (overlap(sw, in_spans[i])) return FUSEDOPS_ERR_INVALID_ARG;
+  }
+
+  // ---- kernel selection
+  Kernel kern;
+  if (in_dtype == FUSEDOPS_F32) {
+    kern = Kernel::F32;
+  } else {
+    const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
+    kern = (M <= 128 && !op_par && big_tiles < 256) ? Kernel::SKINNY : Kernel::T256;
+  }
+  const int tile_rows = kern == Kernel::T256 ? 256 : (kern == Kernel::SKINNY ? 64 : 128);
+  const int tile_tok = kern == Kernel::T256 ? 256 : (kern == Kernel::SKINNY ? 32 : 64);
+  // 32-bit buffer offsets cover one tile's rows
+  if (((int64_t)(tile_rows - 1) * ldw + K) * es_in >= (int64_t(1) << 31) ||
+      ((int64_t)(tile_tok - 1) * ldx + K) * es_in >= (int64_t(1) << 31))
+    return FUSEDOPS_ERR_UNSUPPORTED;
+
+  GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.X = X; a.ldx = ldx; a.W = W; a.ldw = ldw;
+  a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  EpiParams& e = a.ep;
+  e.bias = bias; e.bias_dtype = in_dtype;
+  if (op_res) { e.z = op_res->in; e.ldz = op_res->ld; e.z_dtype = op_res->dtype; }
+  if (op_aux) { e.aux = op_aux->out; e.ld_aux = op_aux->ld; e.aux_dtype = op_aux->dtype; }
+  if (op_par) { e.partials = static_cast<float*>(op_par->out); e.ldp = op_par->ld; }
+  if (op_gam) { e.gamma = op_gam->in; e.gamma_dtype = op_gam->dtype; }
+  if (op_row) e.rscale = static_cast<const float*>(op_row->in);
+  e.act = ol.act;
+  e.quant = ol.quant ? 1 : 0;
+  if (op_q) {
+    e.scales = static_cast<float*>(op_q->out);
+    e.ws = static_cast<uint32_t*>(workspace);
+    e.ws_rb = (int)ws_row_blocks(M);
+  }
+  e.y = Y; e.ldy = ldy; e.y_dtype = out_dtype;
+  if (op_split) {
+    e.n_split = op_split->n_split;
+    e.split_w = N / op_split->n_split;
+    e.ldv = op_split->ld;
+    e.yv0 = op_split->out_v[0];
+    e.yv1 = op_split->out_v[1];
+    e.yv2 = op_split->n_split > 2 ? op_split->out_v[2] : nullptr;
+  }
+
+  // The FP8 row rendezvous needs every column tile of a token block to be able to run
+  // at the same time: check the device can hold that many workgroups at once.
+  if (ol.quant) {
+    const int tile_f = kern == Kernel::T256 ? gemm_bf16_t256_tile_f()
+                       : kern == Kernel::SKINNY ? gemm_bf16_skinny_tile_f() : gemm_f32_tile_f();
+    const void* sym = kern == Kernel::T256 ? gemm_bf16_t256_symbol()
+                      : kern == Kernel::SKINNY ? gemm_bf16_skinny_symbol() : gemm_f32_symbol();
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sym, 256, 0) != hipSuccess)
+      return launch_status(hipErrorInvalidValue, "occupancy query");
+    if (cdiv(N, tile_f) > (int64_t)cus * per_cu) return FUSEDOPS_ERR_UNSUPPORTED;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (kern) {
+    case Kernel::T256: return launch_status(launch_gemm_bf16_t256(a, s), "gemm_bf16_t256");
+    case Kernel::SKINNY: return launch_status(launch_gemm_bf16_skinny(a, s), "gemm_bf16_skinny");
+    default: return launch_status(launch_gemm_f32(a, s), "gemm_f32");
+  }
+}
+
+int32_t fusedops_layernorm_gelu(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows,
+                                int64_t cols, int32_t io_dtype, int32_t out_dtype, const void* gamma,
+                                const void* beta, int32_t param_dtype, float eps, int32_t gelu_form,
+                                void* stream) {
+  if (!x || !y) return FUSEDOPS_ERR_INVALID_ARG;
+  if (rows < 1 || cols < 1) return FUSEDOPS_ERR_INVALID_ARG;
+  if (!valid_dtype(io_dtype) || !valid_dtype(out_dtype)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (!float_dtype(io_dtype) || !float_dtype(out_dtype)) return FUSEDOPS_ERR_UNSUPPORTED;
+  if ((gamma || beta) && !valid_dtype(param_dtype)) return FUSEDOPS_ERR_INVALID_ARG;
+  if ((gamma || beta) && !float_dtype(param_dtype)) return FUSEDOPS_ERR_UNSUPPORTED;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (gelu_form < FUSEDOPS_GELU_NONE || gelu_form > FUSEDOPS_GELU_ERF) return FUSEDOPS_ERR_INVALID_ARG;
+  if (ldx < cols || ldy < cols) return FUSEDOPS_ERR_INVALID_ARG;
+  if (cols > FUSEDOPS_LN_MAX_COLS) return FUSEDOPS_ERR_UNSUPPORTED;
+  if (rows > ((int64_t)1 << 24) - 1) return FUSEDOPS_ERR_UNSUPPORTED;  // grid size bound
+  const int es_in = dtype_size(io_dtype), es_out = dtype_size(out_dtype);
+  const int gran = 16 / es_in;
+  if (cols % gran) return FUSEDOPS_ERR_MISALIGNED;
+  if (!aligned(x, 16) || !aligned(y, 16) || (ldx * es_in) % 16 || (ldy * es_out) % 16) return FUSEDOPS_ERR_MISALIGNED;
+  if ((gamma && !aligned(gamma, 16)) || (beta && !aligned(beta, 16))) return FUSEDOPS_ERR_MISALIGNED;
+  const Span sx = span2d(x, rows, cols, ldx, es_in), sy = span2d(y, rows, cols, ldy, es_out);
+  const int es_p = (gamma || beta) ? dtype_size(param_dtype) : 1;
+  const Span sg = span2d(gamma, 1, cols, cols, es_p), sb = span2d(beta, 1, cols, cols, es_p);
+  const bool inplace = x == y && ldx == ldy && io_dtype == out_dtype;
+  if ((overlap(sy, sx) && !inplace) || overlap(sy, sg) || overlap(sy, sb)) return FUSEDOPS_ERR_INVALID_ARG;
+
+  LnArgs a;
+  a.x = x; a.ldx = ldx; a.y = y; a.ldy = ldy; a.rows = rows; a.cols = (int)cols;
+  a.io_dtype = io_dtype; a.out_dtype = out_dtype; a.gamma = gamma; a.beta = beta;
+  a.param_dtype = param_dtype; a.eps = eps; a.gelu_form = gelu_form;
+  return launch_status(launch_layernorm_gelu(a, static_cast<hipStream_t>(stream)), "layernorm_gelu");
+}
+
+int32_t fusedops_rmsnorm_finalize(const float* partials, int64_t ldp, int64_t M, int64_t T, int64_t N,
+                                  float eps, float* r, const void* h, int64_t ldh, const void* gamma,
+                                  void* y, int64_t ldy, int32_t dtype, void* stream) {
+  if (!partials || !r) return FUSEDOPS_ERR_INVALID_ARG;
+  if (M < 1 || T < 1 || N < 1 || ldp < T) return FUSEDOPS_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return FUSEDOPS_ERR_INVALID_ARG;
+  if ((h == nullptr) != (y == nullptr)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (M > ((int64_t)1 << 26) || T > (1 << 30)) return FUSEDOPS_ERR_UNSUPPORTED;  // grid size bound
+  if (!aligned(partials, 4) || !aligned(r, 4)) return FUSEDOPS_ERR_MISALIGNED;
+  const Span sp = span2d(partials, M, T, ldp, 4), sr = span2d(r, 1, M, M, 4);
+  Span sh, sy, sg;
+  if (h) {
+    if (!valid_dtype(dtype)) return FUSEDOPS_ERR_INVALID_ARG;
+    if (!float_dtype(dtype)) return FUSEDOPS_ERR_UNSUPPORTED;
+    if (ldh < N || ldy < N) return FUSEDOPS_ERR_INVALID_ARG;
+    const int es = dtype_size(dtype);
+    if (N % (16 / es)) return FUSEDOPS_ERR_MISALIGNED;
+    if (!aligned(h, 16) || !aligned(y, 16) || (ldh * es) % 16 || (ldy * es) % 16) return FUSEDOPS_ERR_MISALIGNED;
+    if (gamma && !aligned(gamma, 16)) return FUSEDOPS_ERR_MISALIGNED;
+    sh = span2d(h, M, N, ldh, es);
+    sy = span2d(y, M, N, ldy, es);
+    sg = span2d(gamma, 1, N, N, es);
+    const bool inplace = h == y && ldh == ldy;
+    if ((overlap(sy, sh) && !inplace) || overlap(sy, sg) || overlap(sy, sp)) return FUSEDOPS_ERR_INVALID_ARG;
+  }
+  if (overlap(sr, sp) || overlap(sr, sh) || overlap(sr, sy) || overlap(sr, sg)) return FUSEDOPS_ERR_INVALID_ARG;
+
+  FinalizeArgs a;
+  a.partials = partials; a.ldp = ldp; a.M = M; a.T = (int)T; a.N = N; a.eps = eps; a.r = r;
+  a.h = h; a.ldh = ldh; a.gamma = gamma; a.y = y; a.ldy = ldy; a.dtype = dtype;
+  return launch_status(launch_rmsnorm_finalize(a, static_cast<hipStream_t>(stream)), "rmsnorm_finalize");
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Device-side building blocks shared by the fusedops kernels (gfx950 / CDNA4).
+//
+// Types, fp32 <-> bf16/fp16/fp8 conversions, OOB-safe buffer loads, wave
+// reductions and the activation functions used by the epilogue and the
+// LayerNorm+GELU row kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fusedops.h"
+
+namespace fusedops {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kWave = 64;
+// Third dword of a raw buffer resource on gfx9-family parts (32-bit data
+// format, no swizzle); reads at byte offsets >= num_records return zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// A voffset that is always out of range, so the buffer load returns zero.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buffer_load_16B(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// conversions (round to nearest even everywhere)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even, NaN preserved
+  return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Two fp32 -> two bf16 packed (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return f32_to_f16_bits(a) | (f32_to_f16_bits(b) << 16);
+}
+
+// Two fp32 -> two OCP E4M3 codes (low byte = a); inputs must already be clamped to +-448.
+__device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Load 4 consecutive elements of a 1-D / row vector with a runtime dtype, as fp32.
+// `idx` must be a multiple of 4 (8-byte or 16-byte aligned access).
+__device__ __forceinline__ f32x4 load4(const void* base, int dtype, int64_t idx) {
+  f32x4 r;
+  if (dtype == FUSEDOPS_F32) {
+    r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+  } else {
+    u32x2 v = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + idx);
+    if (dtype == FUSEDOPS_BF16) {
+      r[0] = __uint_as_float(v[0] << 16);
+      r[1] = __uint_as_float(v[0] & 0xFFFF0000u);
+      r[2] = __uint_as_float(v[1] << 16);
+      r[3] = __uint_as_float(v[1] & 0xFFFF0000u);
+    } else {
+      r[0] = f16_bits_to_f32(v[0] & 0xFFFF);
+      r[1] = f16_bits_to_f32(v[0] >> 16);
+      r[2] = f16_bits_to_f32(v[1] & 0xFFFF);
+      r[3] = f16_bits_to_f32(v[1] >> 16);
+    }
+  }
+  return r;
+}
+
+// Store 4 consecutive fp32 values as dtype (not fp8). `idx` multiple of 4.
+__device__ __forceinline__ void store4(void* base, int dtype, int64_t idx, f32x4 v) {
+  if (dtype == FUSEDOPS_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = v;
+  } else if (dtype == FUSEDOPS_BF16) {
+    u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + idx) = o;
+  } else {
+    u32x2 o = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + idx) = o;
+  }
+}
+
+// Store 2 consecutive fp32 values as dtype (not fp8). `idx` multiple of 2.
+__device__ __forceinline__ void store2(void* base, int dtype, int64_t idx, float a, float b) {
+  if (dtype == FUSEDOPS_F32) {
+    float2 o = make_float2(a, b);
+    *reinterpret_cast<float2*>(static_cast<float*>(base) + idx) = o;
+  } else if (dtype == FUSEDOPS_BF16) {
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + idx) = pack_bf16x2(a, b);
+  } else {
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + idx) = pack_f16x2(a, b);
+  }
+}
+
+__device__ __forceinline__ int dtype_bytes(int dtype) {
+  return dtype == FUSEDOPS_F32 ? 4 : (dtype == FUSEDOPS_F8E4M3 ? 1 : 2);
+}
+
+// ---------------------------------------------------------------------------
+// activations (fp32 in registers)
+// ---------------------------------------------------------------------------
+
+// erf for fp32 by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^{-x^2}, t = 1/(1 + p x),
+// x >= 0, absolute error <= 1.5e-7; odd symmetry gives x < 0. Branch-free, one exp and
+// one reciprocal. It also yields 1 + erf(x) for x < 0 without cancellation, which GELU uses.
+__device__ __forceinline__ float erfc_pos_as(float ax) {
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  return poly * __expf(-ax * ax);  // = 1 - erf(ax)
+}
+
+// GELU, erf form: 0.5 v (1 + erf(v / sqrt 2)).
+__device__ __forceinline__ float gelu_erf_f32(float v) {
+  const float u = v * 0.70710678118654752f;
+  const float c = erfc_pos_as(fabsf(u));            // 1 - erf(|u|)
+  const float one_plus_erf = u >= 0.f ? 2.0f - c : c;
+  return 0.5f * v * one_plus_erf;
+}
+
+// GELU, tanh form. 0.5 v (1 + tanh u) equals v / (1 + e^{-2u}), which needs one exp
+// and one reciprocal; u = sqrt(2/pi) (v + 0.044715 v^3).
+__device__ __forceinline__ float gelu_tanh_f32(float v) {
+  const float u = 0.79788456080286536f * (v + 0.044715f * v * v * v);
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+}
+
+// silu(g) = g / (1 + e^-g).
+__device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+// ---------------------------------------------------------------------------
+// wave reductions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+}  // namespace fusedops

@@ -1,0 +1,366 @@
+// The epilogue of the fused linear layer, shared by every GEMM kernel.
+//
+// The contraction is computed transposed, D[f][t] = sum_k W[f][k] X[t][k], with
+// v_mfma_f32_32x32x{16 bf16, 2 f32}. In that instruction's D layout lane l holds
+// column t = l % 32 and rows f = 8 (r / 4) + 4 (l / 32) + (r % 4) of register r: one
+// lane owns one token and runs of four consecutive features, so a wave can drop a
+// block into a token-major LDS tile with 16-byte writes.
+//
+// The finished fp32 accumulator tile is staged in LDS (token-major; 16-byte chunk c of
+// row r sits at chunk position c ^ (r & 15), which keeps both the 16-byte writes from
+// the MFMA layout and the row reads below free of bank conflicts). All 256 threads then
+// run the epilogue chain in a row layout: a thread owns 8 consecutive features of one
+// token, so SwiGLU pairs (2j, 2j+1) sit in the same thread's registers, residual loads
+// and all stores are 16-byte accesses that are contiguous along a row, and a 128-column
+// row partial is a reduction over 16 adjacent lanes.
+//
+// Op order ([Epilogue] §模式A Epilogue 1 / 2, §模式B, §仿射量化与尾声的五步):
+// bias, residual add, store-aux, sum-of-squares partials, column scale, row scale,
+// activation, then FP8 per-row quantisation or a plain / split store.
+#pragma once
+
+#include "common.h"
+
+namespace fusedops {
+
+enum Act { ACT_NONE = 0, ACT_GELU_ERF = 1, ACT_GELU_TANH = 2, ACT_SWIGLU = 3 };
+
+struct EpiParams {
+  const void* bias;       int bias_dtype;
+  const void* z;          int64_t ldz;     int z_dtype;
+  void* aux;              int64_t ld_aux;  int aux_dtype;
+  float* partials;        int64_t ldp;
+  const void* gamma;      int gamma_dtype;
+  const float* rscale;
+  int act;
+  int quant;              // FP8 per-row quantised writeback
+  float* scales;
+  uint32_t* ws;           // rendezvous workspace (quant only)
+  int ws_rb;              // row-block counters reserved in the workspace
+  void* y;                int64_t ldy;     int y_dtype;
+  int n_split;            int64_t split_w; int64_t ldv;
+  void* yv0;              void* yv1;       void* yv2;
+};
+
+struct GemmArgs {
+  const void* X; int64_t ldx;
+  const void* W; int64_t ldw;
+  int M, N, K;
+  int tiles_t, tiles_f;   // token tiles x feature tiles
+  EpiParams ep;
+};
+
+constexpr int kEpiThreads = 256;
+
+// ---------------------------------------------------------------------------
+// FP8 row rendezvous
+// ---------------------------------------------------------------------------
+// Workspace layout (uint32 words):
+//   [0]                error word: set to 1 if a wait ever hit its spin bound (never cleared here)
+//   [1]                tile ticket counter
+//   [2, 2+R)           arrivals per row block
+//   [2+R, 2+2R)        departures per row block
+//   [2+2R, 2+2R+M)     per-row absmax as float bits (non-negative floats order like uint32)
+// Every word except [0] is back at zero when the kernel ends.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__device__ __forceinline__ uint32_t* ws_arrive(uint32_t* ws) { return ws + 2; }
+__device__ __forceinline__ uint32_t* ws_depart(uint32_t* ws, int R) { return ws + 2 + R; }
+__device__ __forceinline__ uint32_t* ws_amax(uint32_t* ws, int R) { return ws + 2 + 2 * R; }
+
+// Take the next tile ticket (thread 0 draws, the block shares it through LDS). The block
+// that draws the last ticket resets the counter: every other ticket was already drawn.
+__device__ __forceinline__ int draw_ticket(uint32_t* ws, int total, int* lds_slot) {
+  if (threadIdx.x == 0) {
+    uint32_t t = __hip_atomic_fetch_add(ws + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)t == total - 1)
+      __hip_atomic_store(ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_slot = (int)t;
+  }
+  __syncthreads();
+  int t = *lds_slot;
+  __syncthreads();
+  return t;
+}
+
+// Arrive at row block `rb` and wait until all `need` tiles of it have arrived. Every
+// tile publishes its absmax contribution before arriving, so once the count is complete
+// the per-row maxima are final. The wait is bounded; on timeout the error word is set.
+__device__ __forceinline__ void rendezvous_wait(uint32_t* ws, int rb, int need) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t* arrive = ws_arrive(ws) + rb;
+    __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t it = 0;
+    while (__hip_atomic_load(arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)need) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++it > kSpinLimit) {
+        __hip_atomic_store(ws, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  __threadfence();
+}
+
+// Leave row block `rb`; the last tile to leave clears the block's counters and the absmax
+// of its rows [t0, t0 + ntok) so the workspace is zero again for the next call.
+__device__ __forceinline__ void rendezvous_depart(uint32_t* ws, int R, int rb, int need, int t0,
+                                                  int ntok, int* lds_slot) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t old = __hip_atomic_fetch_add(ws_depart(ws, R) + rb, 1u, __ATOMIC_ACQ_REL,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    *lds_slot = (old == (uint32_t)need - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*lds_slot) {
+    uint32_t* amax = ws_amax(ws, R);
+    for (int i = threadIdx.x; i < ntok; i += blockDim.x)
+      __hip_atomic_store(amax + t0 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(ws_arrive(ws) + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ws_depart(ws, R) + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// staged tile
+// ---------------------------------------------------------------------------
+
+// Float offset of element (r, c) of a token-major fp32 tile with COLS columns
+// (c a multiple of 4 for 16-byte accesses).
+template <int COLS>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  static_assert(COLS % 64 == 0, "rows must span at least 16 chunks");
+  return r * COLS + ((((c >> 2) ^ (r & 15))) << 2) + (c & 3);
+}
+
+// Write one 32 x 32 MFMA D block (features f_loc.., tokens r_loc..) into the tile.
+template <int COLS>
+__device__ __forceinline__ void stage_block(float* tile, const f32x16& d, int f_loc, int r_loc) {
+  const int lane = threadIdx.x & 63;
+  const int r = r_loc + (lane & 31);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = f_loc + q * 8 + (lane >> 5) * 4;
+    *reinterpret_cast<f32x4*>(tile + tile_off<COLS>(r, c)) = f32x4{d[q * 4], d[q * 4 + 1], d[q * 4 + 2], d[q * 4 + 3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 8-wide loads / stores with a runtime dtype
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void load8(const void* base, int dtype, int64_t idx, float (&o)[8]) {
+  if (dtype == FUSEDOPS_F32) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx + 4);
+    o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
+    o[4] = b[0]; o[5] = b[1]; o[6] = b[2]; o[7] = b[3];
+  } else {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (dtype == FUSEDOPS_BF16) {
+        o[2 * j] = __uint_as_float(v[j] << 16);
+        o[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
+      } else {
+        o[2 * j] = f16_bits_to_f32(v[j] & 0xFFFF);
+        o[2 * j + 1] = f16_bits_to_f32(v[j] >> 16);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void store8(void* base, int dtype, int64_t idx, const float (&v)[8]) {
+  if (dtype == FUSEDOPS_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = dtype == FUSEDOPS_BF16 ? pack_bf16x2(v[2 * j], v[2 * j + 1]) : pack_f16x2(v[2 * j], v[2 * j + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + idx) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the chain over a staged tile
+// ---------------------------------------------------------------------------
+
+enum EpiMode {
+  EPI_STORE = 0,  // chain + side outputs + main store
+  EPI_AMAX = 1,   // chain + side outputs + per-row absmax published to the workspace
+  EPI_QUANT = 2,  // chain (no side outputs) + FP8 quantisation with the final row scales
+};
+
+// Run the epilogue over rows [0, nrows) of a staged tile whose element (r, c) is the
+// accumulator of token t0 + r and feature f0 + c. NSRC tiles (each ROWS_ALLOC x COLS) are
+// summed element-wise first, in order (used to merge split-K partial sums). Every thread
+// of the block must call this (it contains wave-wide shuffles but no barriers).
+template <int COLS, int NSRC, int ROWS_ALLOC>
+__device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* tile, int t0,
+                                              int nrows, int f0, int mode) {
+  constexpr int TPR = COLS / 8;            // threads per row
+  constexpr int RPI = kEpiThreads / TPR;   // rows per iteration
+  static_assert(TPR <= 64 && 64 % TPR == 0, "a row's threads must sit in one wave");
+  const EpiParams& e = a.ep;
+  const int M = a.M, N = a.N;
+  const int tid = threadIdx.x;
+  const int g = tid % TPR;
+  const int c = g * 8;
+  const int f = f0 + c;
+  const bool f_ok = f < N;
+  const bool swiglu = e.act == ACT_SWIGLU;
+  const bool side = mode != EPI_QUANT;
+  const int zb = e.z_dtype == FUSEDOPS_F32 ? 4 : 2;
+  const int ab = e.aux_dtype == FUSEDOPS_F32 ? 4 : 2;
+  const int yb = e.y_dtype == FUSEDOPS_F32 ? 4 : (e.y_dtype == FUSEDOPS_F8E4M3 ? 1 : 2);
+
+  // per-feature vectors, loaded once per pass
+  float bias[8], gam[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { bias[i] = 0.f; gam[i] = 1.f; }
+  if (e.bias && f_ok) load8(e.bias, e.bias_dtype, f, bias);
+  if (e.gamma && f_ok) load8(e.gamma, e.gamma_dtype, f, gam);
+
+  for (int r = tid / TPR; r < nrows; r += RPI) {
+    const int t = t0 + r;
+    const bool t_ok = t < M;
+    const bool ok = t_ok && f_ok;
+    float v[8];
+    {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(tile + tile_off<COLS>(r, c));
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(tile + tile_off<COLS>(r, c + 4));
+      v[0] = a0[0]; v[1] = a0[1]; v[2] = a0[2]; v[3] = a0[3];
+      v[4] = a1[0]; v[5] = a1[1]; v[6] = a1[2]; v[7] = a1[3];
+#pragma unroll
+      for (int s = 1; s < NSRC; ++s) {
+        const float* ts = tile + s * ROWS_ALLOC * COLS;
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(ts + tile_off<COLS>(r, c));
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(ts + tile_off<COLS>(r, c + 4));
+        v[0] += b0[0]; v[1] += b0[1]; v[2] += b0[2]; v[3] += b0[3];
+        v[4] += b1[0]; v[5] += b1[1]; v[6] += b1[2]; v[7] += b1[3];
+      }
+    }
+    // bias, residual
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += bias[i];
+    if (e.z && ok) {
+      float z[8];
+      load8(static_cast<const char*>(e.z) + (int64_t)t * e.ldz * zb, e.z_dtype, f, z);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += z[i];
+    }
+    // store-aux (h1) and its row sum-of-squares partials over 128-column chunks
+    if (side && e.aux && ok) store8(static_cast<char*>(e.aux) + (int64_t)t * e.ld_aux * ab, e.aux_dtype, f, v);
+    if (COLS >= 128 && e.partials) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i] * v[i];
+      // 16 adjacent lanes = 128 columns; columns >= N hold exact zeros
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, kWave);
+      if (side && t_ok && (g & 15) == 0 && f_ok) e.partials[(int64_t)t * e.ldp + f / 128] = s;
+    }
+    // column scale, row scale
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= gam[i];
+    if (e.rscale) {
+      const float rs = t_ok ? e.rscale[t] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] *= rs;
+    }
+    // activation; SwiGLU leaves its 4 outputs in v[0..3]
+    if (e.act == ACT_GELU_ERF) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = gelu_erf_f32(v[i]);
+    } else if (e.act == ACT_GELU_TANH) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = gelu_tanh_f32(v[i]);
+    } else if (swiglu) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = silu_f32(v[2 * j]) * v[2 * j + 1];
+#pragma unroll
+      for (int j = 4; j < 8; ++j) v[j] = 0.f;
+    }
+    const int fo = swiglu ? f / 2 : f;  // output column of v[0]
+
+    if (mode == EPI_STORE) {
+      if (!ok) continue;
+      if (swiglu) {
+        store4(static_cast<char*>(e.y) + (int64_t)t * e.ldy * yb, e.y_dtype, fo, f32x4{v[0], v[1], v[2], v[3]});
+      } else if (e.n_split) {
+        const int seg = (int)(f / e.split_w);
+        void* base = seg == 0 ? e.yv0 : (seg == 1 ? e.yv1 : e.yv2);
+        store8(static_cast<char*>(base) + (int64_t)t * e.ldv * yb, e.y_dtype, f - (int64_t)seg * e.split_w, v);
+      } else {
+        store8(static_cast<char*>(e.y) + (int64_t)t * e.ldy * yb, e.y_dtype, f, v);
+      }
+    } else if (mode == EPI_AMAX) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+      if (!f_ok) m = 0.f;
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+      if (g == 0 && t_ok)
+        __hip_atomic_fetch_max(ws_amax(e.ws, e.ws_rb) + t, __float_as_uint(m), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (!t_ok) continue;
+      const float amax = __uint_as_float(
+          __hip_atomic_load(ws_amax(e.ws, e.ws_rb) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      const float s = __fdiv_rn(amax, 448.0f);  // IEEE division: s = fl32(a / 448)
+      const float inv = s > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+      if (f0 == 0 && g == 0) e.scales[t] = s;
+      if (!f_ok) continue;
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(v[i] * inv, -448.f), 448.f);
+      uint8_t* yrow = static_cast<uint8_t*>(e.y) + (int64_t)t * e.ldy;
+      if (swiglu) {
+        *reinterpret_cast<uint32_t*>(yrow + fo) = pack_e4m3x2(q[0], q[1]) | (pack_e4m3x2(q[2], q[3]) << 16);
+      } else {
+        const u32x2 w = {pack_e4m3x2(q[0], q[1]) | (pack_e4m3x2(q[2], q[3]) << 16),
+                         pack_e4m3x2(q[4], q[5]) | (pack_e4m3x2(q[6], q[7]) << 16)};
+        *reinterpret_cast<u32x2*>(yrow + fo) = w;
+      }
+    }
+  }
+}
+
+// Drive the epilogue for one tile held in registers, staging PASSES token slices through
+// LDS. `stage(pass, tile)` must write this pass's accumulator blocks into the tile (it is
+// called by every wave; waves that own nothing in a pass write nothing). The tile origin
+// is (t0, f0) and each pass covers ROWS tokens (`nrows_total` valid tokens in the tile).
+// For FP8 row quantisation the chain runs twice: first to publish the row absmax, then,
+// after every column tile of the token block has done so, to quantise.
+template <int COLS, int NSRC, int ROWS, int PASSES, typename StageFn>
+__device__ __forceinline__ void run_staged_epilogue(const GemmArgs& a, float* tile, int t0, int f0,
+                                                    int nrows_total, int rb, int* lds_slot,
+                                                    StageFn&& stage) {
+  const EpiParams& e = a.ep;
+  const int rounds = e.quant ? 2 : 1;
+  for (int round = 0; round < rounds; ++round) {
+    if (round == 1) rendezvous_wait(e.ws, rb, a.tiles_f);
+    const int mode = e.quant ? (round == 0 ? EPI_AMAX : EPI_QUANT) : EPI_STORE;
+    for (int p = 0; p < PASSES; ++p) {
+      const int rows = min(ROWS, nrows_total - p * ROWS);
+      if (rows <= 0) break;
+      __syncthreads();
+      stage(p, tile);
+      __syncthreads();
+      epilogue_pass<COLS, NSRC, ROWS>(a, tile, t0 + p * ROWS, rows, f0, mode);
+    }
+  }
+  if (e.quant) rendezvous_depart(e.ws, e.ws_rb, rb, a.tiles_f, t0, nrows_total, lds_slot);
+}
+
+}  // namespace fusedops

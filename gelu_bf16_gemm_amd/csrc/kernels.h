@@ -1,0 +1,53 @@
+// Host-side launchers of the fusedops kernels (internal; the public surface is fusedops.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fusedops {
+
+struct GemmArgs;
+
+// bf16 GEMM + epilogue, 256 x 256 tiles (tokens x features), 4 waves.
+hipError_t launch_gemm_bf16_t256(GemmArgs a, hipStream_t stream);
+int gemm_bf16_t256_tile_t();
+int gemm_bf16_t256_tile_f();
+const void* gemm_bf16_t256_symbol();
+
+// bf16 GEMM + epilogue for few tokens (decode): 32-token x 64-feature tiles, K split
+// over the 4 waves.
+hipError_t launch_gemm_bf16_skinny(GemmArgs a, hipStream_t stream);
+int gemm_bf16_skinny_tile_t();
+int gemm_bf16_skinny_tile_f();
+const void* gemm_bf16_skinny_symbol();
+
+// fp32 GEMM + epilogue (v_mfma_f32_32x32x2_f32), 64-token x 128-feature tiles.
+hipError_t launch_gemm_f32(GemmArgs a, hipStream_t stream);
+int gemm_f32_tile_t();
+int gemm_f32_tile_f();
+const void* gemm_f32_symbol();
+
+struct LnArgs {
+  const void* x; int64_t ldx;
+  void* y; int64_t ldy;
+  int64_t rows; int cols;
+  int io_dtype, out_dtype;
+  const void* gamma; const void* beta; int param_dtype;
+  float eps;
+  int gelu_form;
+};
+hipError_t launch_layernorm_gelu(const LnArgs& a, hipStream_t stream);
+
+struct FinalizeArgs {
+  const float* partials; int64_t ldp;
+  int64_t M; int T; int64_t N;
+  float eps;
+  float* r;
+  const void* h; int64_t ldh;
+  const void* gamma;
+  void* y; int64_t ldy;
+  int dtype;
+};
+hipError_t launch_rmsnorm_finalize(const FinalizeArgs& a, hipStream_t stream);
+
+}  // namespace fusedops

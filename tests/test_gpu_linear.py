@@ -1,0 +1,326 @@
+"""Parity of the fused linear layer (HIP path through the C ABI) with the fp64 oracle.
+
+Shapes span several tiles of each kernel and end in ragged tiles (M, N, K off the
+tile grid), as the layout-contract check on the GEMM-epilogue page asks for the last
+incomplete tile. Every output sits inside a guard band that must stay untouched.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gelu_bf16_gemm_amd import inputs as I
+
+from helpers import Guarded, check_f32, check_fp8, check_lowp, check_out, dev, host64, note
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gelu_bf16_gemm_amd import binding as B  # noqa: E402  (fails loudly if the library is missing)
+
+ACT_OP = {"gelu_erf": B.OP_GELU_ERF, "gelu_tanh": B.OP_GELU_TANH, "swiglu": B.OP_SWIGLU}
+
+
+def upload_padded(stored, dtype, pad):
+    """Device copy with `pad` extra columns (leading dimension cols + pad)."""
+    rows, cols = stored.shape
+    if pad == 0:
+        return dev(stored, dtype)
+    full = np.zeros((rows, cols + pad), dtype=stored.dtype)
+    full[:, :cols] = stored
+    return dev(full, dtype)[:, :cols]
+
+
+def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=None, residual=False,
+               aux=False, partials=False, gamma=False, rscale=False, split=0, quant=False, seed=0,
+               pad=0, inplace=False, aux_dtype=None, z_dtype=None, check=True):
+    rng = np.random.default_rng([101, M, N, K, seed])
+    X = I.random_stored(rng, (M, K), in_dtype)
+    W = I.random_stored(rng, (N, K), in_dtype, std=1 / math.sqrt(K))
+    b = I.random_stored(rng, (N,), in_dtype, std=0.5) if bias else None
+    zdt = z_dtype if z_dtype is not None else (I.BF16 if in_dtype == I.BF16 else in_dtype)
+    z = I.random_stored(rng, (M, N), zdt) if residual else None
+    g = I.random_stored(rng, (N,), zdt, mean=1.0, std=0.1) if gamma else None
+    r = rng.uniform(0.5, 1.5, M).astype(np.float32) if rscale else None
+
+    note(f"linear M={M} N={N} K={K} in={in_dtype} out={out_dtype} act={act} bias={bias} res={residual} "
+         f"aux={aux} partials={partials} gamma={gamma} rscale={rscale} split={split} quant={quant} "
+         f"pad={pad} inplace={inplace} seed={seed}")
+    Xd = upload_padded(X, in_dtype, pad)
+    Wd = upload_padded(W, in_dtype, pad)
+    bd = dev(b, in_dtype) if bias else None
+    n_out = N // 2 if act == "swiglu" else N
+    ops, keep = [], {}
+    if residual:
+        if inplace:
+            zg = Guarded(M, N, zdt)
+            zg.view.copy_(dev(z, zdt))
+            keep["z"] = zg
+            ops.append(B.op(B.OP_RESIDUAL_ADD, zg.view))
+        else:
+            keep["z"] = dev(z, zdt)
+            ops.append(B.op(B.OP_RESIDUAL_ADD, keep["z"]))
+    if aux:
+        keep["aux"] = Guarded(M, N, aux_dtype if aux_dtype is not None else zdt)
+        ops.append(B.op(B.OP_STORE_AUX, out=keep["aux"].view))
+    if partials:
+        T = -(-N // 128)
+        keep["p"] = Guarded(M, T, I.F32, ld=T + 4)
+        ops.append(B.op(B.OP_ROWSUMSQ_PARTIAL, out=keep["p"].view))
+    if gamma:
+        keep["g"] = dev(g, zdt)
+        ops.append(B.op(B.OP_COL_SCALE, keep["g"]))
+    if rscale:
+        keep["r"] = dev(r, I.F32)
+        ops.append(B.op(B.OP_ROW_SCALE, keep["r"]))
+    if act:
+        ops.append(B.op(ACT_OP[act]))
+    ws = None
+    if quant:
+        keep["s"] = Guarded(1, M, I.F32)
+        ops.append(B.op(B.OP_QUANT_FP8_ROW, out=keep["s"].view[0]))
+        nbytes = B.fusedops_linear_workspace_bytes(M, N, K, ops)
+        ws = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    if split:
+        keep["split"] = [Guarded(M, N // split, out_dtype) for _ in range(split)]
+        ops.append(B.op(B.OP_SPLIT_COLS, split=[s.view for s in keep["split"]]))
+        y = None
+    elif inplace:
+        y = keep["z"]
+    else:
+        y = Guarded(M, n_out, I.F8E4M3 if quant else out_dtype)
+    st = B.fusedops_linear_epilogue(Xd, Wd, y.view if y is not None else None, bias=bd, ops=ops,
+                                    workspace=ws, out_dtype=I.F8E4M3 if quant else out_dtype)
+    assert st == B.OK, B.status_string(st)
+    torch.cuda.synchronize()
+
+    ref = O.linear_epilogue(I.to_f64(X, in_dtype), I.to_f64(W, in_dtype),
+                            bias=None if b is None else I.to_f64(b, in_dtype),
+                            residual=None if z is None else I.to_f64(z, zdt),
+                            col_scale=None if g is None else I.to_f64(g, zdt),
+                            row_scale=None if r is None else r.astype(np.float64), act=act)
+    out = {"ref": ref, "keep": keep, "y": y, "ws": ws, "X": X, "W": W}
+    if not check:
+        return out
+    if y is not None:
+        assert y.intact(), "guard band of Y overwritten"
+    if quant:
+        s = host64(keep["s"].view[0]).astype(np.float32)
+        assert keep["s"].intact()
+        check_fp8(host64(y.view), s, ref["y"], "fp8 codes")
+        # scale vs the oracle's row absmax: within the fp32 accumulation bound
+        a_ref = np.abs(ref["y"]).max(axis=1)
+        s_ref = O.fp8_row_scale(a_ref).astype(np.float64)
+        np.testing.assert_allclose(s.astype(np.float64), s_ref, rtol=2e-4, atol=1e-30)
+        assert int(ws.abs().sum().item()) == 0, "workspace not left zero-filled"
+    elif split:
+        d = N // split
+        for i, sg in enumerate(keep["split"]):
+            assert sg.intact()
+            check_out(host64(sg.view), ref["y"][:, i * d:(i + 1) * d], out_dtype, f"split block {i}")
+    else:
+        check_out(host64(y.view), ref["y"], out_dtype, "Y")
+    if aux:
+        adt = aux_dtype if aux_dtype is not None else zdt
+        assert keep["aux"].intact()
+        check_out(host64(keep["aux"].view), ref["h1"], adt, "aux h1")
+    if partials:
+        assert keep["p"].intact()
+        check_f32(host64(keep["p"].view), ref["partials"], "row partials")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# shapes: (300, 264, 136) -> 2 x 2 tiles of the 256-tile kernel, all ragged;
+# (17, 72, 40) and (32, 2048, 256) -> the few-token kernel; (1, 8, 8) the smallest.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 136), (17, 72, 40), (1, 8, 8), (129, 512, 64), (520, 776, 264)])
+def test_bias_gelu_erf_bf16(M, N, K):
+    run_linear(M, N, K, bias=True, act="gelu_erf")
+
+
+@pytest.mark.parametrize("out_dtype", [I.F16, I.F32])
+def test_out_dtypes(out_dtype):
+    run_linear(300, 264, 136, bias=True, act="gelu_erf", out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 136), (17, 72, 40)])
+def test_gelu_tanh_and_plain(M, N, K):
+    run_linear(M, N, K, bias=True, act="gelu_tanh")
+    run_linear(M, N, K, act=None, seed=1)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 528, 136), (17, 528, 72), (64, 2048, 256)])
+def test_swiglu(M, N, K):
+    run_linear(M, N, K, act="swiglu")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 392, 136), (64, 256, 72)])
+def test_residual_aux_partials_gamma(M, N, K):
+    out = run_linear(M, N, K, residual=True, aux=True, partials=True, gamma=True)
+    # finalize over the GPU's own partials and over the oracle's
+    p = out["keep"]["p"].view
+    r = torch.empty(M, dtype=torch.float32, device="cuda")
+    note(f"finalize M={M} N={N}")
+    assert B.fusedops_rmsnorm_finalize(p, N, 1e-6, r) == B.OK
+    torch.cuda.synchronize()
+    check_f32(host64(r), O.rmsnorm_finalize(host64(p), N, 1e-6), "r from GPU partials")
+    check_f32(host64(r), O.rmsnorm_finalize(out["ref"]["partials"], N, 1e-6), "r from oracle partials")
+
+
+def test_residual_in_place_and_padded_strides():
+    run_linear(300, 264, 136, residual=True, gamma=True, inplace=True, pad=24)
+    run_linear(17, 72, 40, bias=True, act="gelu_erf", pad=8, seed=2)
+
+
+def test_residual_f32_aux_f16():
+    run_linear(300, 264, 136, residual=True, aux=True, partials=True, z_dtype=I.F32, aux_dtype=I.F16,
+               out_dtype=I.F32)
+
+
+def test_row_scale():
+    run_linear(300, 264, 136, rscale=True, act="gelu_tanh")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 408, 136), (17, 408, 40)])
+def test_split_qkv(M, N, K):
+    run_linear(M, N, K, bias=True, split=3)
+
+
+def test_qkv_split_scaled_blocks_bit_exact():
+    """W_qkv = [A; 2A; 4A], b = [c; 2c; 4c]: power-of-two scaling commutes with rounding, so the
+    K block is exactly 2 Q and the V block exactly 4 Q (the QKV split of the operator-fusion page)."""
+    M, d, K = 300, 136, 136
+    rng = np.random.default_rng(7)
+    A = I.random_stored(rng, (d, K), I.BF16, std=1 / math.sqrt(K))
+    c = I.random_stored(rng, (d,), I.BF16, std=0.5)
+    A32 = I.bf16_bits_to_f32(A)
+    c32 = I.bf16_bits_to_f32(c)
+    W = I.f32_to_bf16_bits(np.vstack([A32, 2 * A32, 4 * A32]))
+    b = I.f32_to_bf16_bits(np.concatenate([c32, 2 * c32, 4 * c32]))
+    X = I.random_stored(rng, (M, K), I.BF16)
+    outs = [Guarded(M, d, I.F32) for _ in range(3)]
+    note("qkv scaled blocks")
+    st = B.fusedops_linear_epilogue(dev(X, I.BF16), dev(W, I.BF16), None, bias=dev(b, I.BF16),
+                                    ops=[B.op(B.OP_SPLIT_COLS, split=[o.view for o in outs])], out_dtype=I.F32)
+    assert st == B.OK
+    torch.cuda.synchronize()
+    q, k, v = (host64(o.view) for o in outs)
+    assert np.array_equal(k, 2 * q) and np.array_equal(v, 4 * q)
+    ref = O.linear_epilogue(I.to_f64(X, I.BF16), I.to_f64(W, I.BF16), bias=I.to_f64(b, I.BF16))["y"]
+    check_f32(np.hstack([q, k, v]), ref, "qkv f32")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 528, 136), (17, 528, 72), (32, 2048, 256), (600, 1040, 64)])
+def test_swiglu_fp8_rows(M, N, K):
+    out = run_linear(M, N, K, act="swiglu", quant=True)
+    # tier 2: the same kernel with an fp32 output gives the pre-quantisation values;
+    # the scale must be exactly fl32(max|y32| / 448) and the codes within 1 ulp of them
+    y32 = run_linear(M, N, K, act="swiglu", out_dtype=I.F32, seed=0, check=False)["y"]
+    y32 = host64(y32.view)
+    check_f32(y32, out["ref"]["y"], "pre-quantisation values")
+    s = host64(out["keep"]["s"].view[0]).astype(np.float32)
+    a_gpu = np.abs(y32).max(axis=1).astype(np.float32)
+    assert np.array_equal(s, O.fp8_row_scale(a_gpu)), "scale is not fl32(absmax / 448)"
+    check_fp8(host64(out["y"].view), s, y32, "codes vs own fp32 values")
+    codes = host64(out["y"].view)
+    assert all(((codes[m] & 0x7F) == 0x7E).any() for m in range(M) if s[m] > 0)
+
+
+def test_fp8_rows_without_activation():
+    run_linear(300, 264, 136, bias=True, quant=True)
+
+
+def test_fp8_tier1_exact_scales_and_codes():
+    """Integer-valued rows and W = I: every pre-quantisation value is exact, so the scales
+    must equal the oracle's bit for bit and the codes must be E4M3 round-to-nearest-even of
+    the exact quotients, including ties (midpoints between neighbouring E4M3 values)."""
+    M, K = 40, 64
+    N = K
+    vals = O.e4m3_values()[:0x7F]
+    mids = (vals[:-1] + vals[1:]) / 2                        # exact in bf16 (<= 5 significant bits)
+    rng = np.random.default_rng(8)
+    X32 = np.zeros((M, K), np.float32)
+    for m in range(M):
+        if m == M - 1:
+            continue                                         # an all-zero row: s = 0, codes 0
+        row = rng.choice(np.concatenate([vals, mids, -vals, -mids]), size=K)
+        row[rng.integers(K)] = 448.0 if m % 2 == 0 else -448.0
+        if m % 5 == 1:
+            row = row / 2                                    # absmax 224: s = 0.5, still exact
+        X32[m] = row
+    X = I.f32_to_bf16_bits(X32)
+    assert np.array_equal(I.bf16_bits_to_f32(X), X32)
+    W = I.f32_to_bf16_bits(np.eye(N, K, dtype=np.float32))
+    y = Guarded(M, N, I.F8E4M3)
+    s = torch.full((M,), -1.0, dtype=torch.float32, device="cuda")
+    ops = [B.op(B.OP_QUANT_FP8_ROW, out=s)]
+    ws = torch.zeros(B.fusedops_linear_workspace_bytes(M, N, K, ops) // 4, dtype=torch.int32, device="cuda")
+    note("fp8 tier 1")
+    assert B.fusedops_linear_epilogue(dev(X, I.BF16), dev(W, I.BF16), y.view, ops=ops, workspace=ws,
+                                      out_dtype=I.F8E4M3) == B.OK
+    torch.cuda.synchronize()
+    s_ref = O.fp8_row_scale(np.abs(X32.astype(np.float64)).max(1))
+    assert np.array_equal(host64(s).astype(np.float32), s_ref)
+    q_ref = O.quantize_fp8_rows(X32.astype(np.float64), s_ref)
+    got = host64(y.view)
+    # equal on the E4M3 value line (the contraction turns -0 inputs into +0, so the sign of
+    # zero is not compared)
+    bad = np.argwhere(O.e4m3_ordinal(got) != O.e4m3_ordinal(q_ref))
+    assert bad.size == 0, f"{len(bad)} codes differ: " + ", ".join(
+        f"v={X32[m, j] / s_ref[m]!r} gpu={got[m, j]:#04x} ref={q_ref[m, j]:#04x}" for m, j in bad[:10])
+    assert y.intact()
+    assert int(ws.abs().sum().item()) == 0
+
+
+def test_fp32_linear_gelu_full_size():
+    """The fp32 workload at its full size: X 64x256, W 256x256, b 256, GELU(erf)."""
+    spec = I.WORKLOADS["linear_gelu_f32_64x256x256"]
+    inp = I.make_linear_inputs(spec)
+    y = Guarded(64, 256, I.F32)
+    note("fp32 linear gelu 64x256x256")
+    st = B.fusedops_linear_epilogue(dev(inp["X"], I.F32), dev(inp["W"], I.F32), y.view,
+                                    bias=dev(inp["b"], I.F32), ops=[B.op(B.OP_GELU_ERF)])
+    assert st == B.OK
+    torch.cuda.synchronize()
+    ref = O.linear_epilogue(inp["X"], inp["W"], bias=inp["b"], act="gelu_erf")["y"]
+    check_f32(host64(y.view), ref, "fp32 Y")
+    assert y.intact()
+
+
+@pytest.mark.parametrize("M,N,K", [(70, 136, 36), (1, 8, 4)])
+def test_fp32_path_ops(M, N, K):
+    run_linear(M, N, K, in_dtype=I.F32, out_dtype=I.F32, bias=True, residual=True, aux=True, partials=True,
+               gamma=True, act="gelu_erf")
+    run_linear(M, N, K, in_dtype=I.F32, out_dtype=I.F32, act="swiglu", quant=True, seed=3)
+
+
+def test_repeatable_bitwise():
+    a = run_linear(300, 264, 136, bias=True, act="gelu_erf", check=False)["y"]
+    b = run_linear(300, 264, 136, bias=True, act="gelu_erf", check=False)["y"]
+    assert torch.equal(a.view, b.view)
+
+
+def test_finalize_apply_mode():
+    M, N = 70, 392
+    rng = np.random.default_rng(9)
+    T = -(-N // 128)
+    p = rng.uniform(0.1, 5.0, (M, T)).astype(np.float32) * N / T
+    h = I.random_stored(rng, (M, N), I.BF16)
+    g = I.random_stored(rng, (N,), I.BF16, mean=1.0, std=0.1)
+    pd = dev(p, I.F32)
+    r = torch.empty(M, dtype=torch.float32, device="cuda")
+    y = Guarded(M, N, I.BF16)
+    note("finalize apply")
+    assert B.fusedops_rmsnorm_finalize(pd, N, 1e-6, r, h=dev(h, I.BF16), gamma=dev(g, I.BF16), y=y.view) == B.OK
+    torch.cuda.synchronize()
+    r_ref = O.rmsnorm_finalize(p, N, 1e-6)
+    check_f32(host64(r), r_ref, "r")
+    check_lowp(host64(y.view), O.rmsnorm_apply(r_ref, I.to_f64(h, I.BF16), I.to_f64(g, I.BF16)), "applied")
+    assert y.intact()
