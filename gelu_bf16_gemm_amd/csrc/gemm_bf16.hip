@@ -3,17 +3,20 @@
 // Mainloop ([Fusion] §Linear算子剖析; [Epilogue] §主循环与尾声): one workgroup of
 // 4 waves owns a 256-feature x 256-token output tile and walks K in steps of 64.
 // Each step's W and X tiles (256 rows x 64 bf16, both K-contiguous in HBM) are
-// staged in LDS, double buffered: the next step's 16-byte global loads are in
-// flight in registers while the MFMAs of the current step run, and are written
-// to the other LDS buffer afterwards, so each step needs one barrier.
+// staged in LDS, double buffered, with two register stage sets in front: during
+// step s the MFMAs read LDS buffer s&1 while the data of step s+1 (already in
+// registers) is written to the other buffer and the 16-byte global loads of step
+// s+2 are issued; MFMAs, operand reads, fills and loads are interleaved so that
+// the single wave per SIMD always has matrix work queued. One barrier per step.
 //
-// LDS layout: a 64-wide K tile row is 128 bytes = 8 chunks of 16 bytes; chunk c
-// of row r is stored at chunk position c ^ (r & 7). Eight consecutive rows read
-// at the same logical chunk then hit 8 different 16-byte bank groups, so the
-// ds_read_b128 operand fetches and the ds_write_b128 fills are conflict-free.
+// LDS layout: a 64-wide K tile row is 128 bytes = 8 chunks of 16 bytes, XOR-swizzled
+// per row (see swz) so the ds_read_b128 operand fetches and the ds_write_b128
+// fills are free of bank conflicts.
 //
 // Each wave computes 128 features x 128 tokens as 4 x 4 v_mfma_f32_32x32x16_bf16
 // blocks (A = W rows, B = X rows, D[f][t]); the epilogue then stages the tile in LDS.
+#include <type_traits>
+
 #include "epilogue.h"
 #include "kernels.h"
 
@@ -27,8 +30,13 @@ constexpr int BK = 64;    // K per step
 constexpr int kThreads = 256;
 constexpr int kTileBytes = 256 * BK * 2;  // one operand tile in LDS (32 KB)
 
+// 16-byte chunk `chunk` of LDS row `row` sits at chunk position chunk ^ f(row) with
+// f(row) = (row & 7) ^ ((row >> 3) & 1): any 8 consecutive rows at one logical chunk use 8
+// distinct positions (128-byte bank window) and any 16 consecutive rows use 16 distinct
+// (position, row parity) pairs (256-byte bank window), for reads and fills alike.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+  return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
 }
 
 // Map a linear tile id to (token tile, feature tile). Consecutive workgroups are
@@ -81,32 +89,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
 
   // Global->LDS assignment: 8 chunks per thread per operand; chunk id j*256 + tid is
   // row j*32 + tid/8, 16-byte chunk tid%8 (8 threads read one 128-byte row segment).
+  // The per-lane part of the address is a VGPR; the j*32-row part is a scalar offset.
   const int ld_row = tid >> 3, ld_c = tid & 7;
-  uint32_t w_voff[8], x_voff[8], st_off[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = j * 32 + ld_row;
-    w_voff[j] = (uint32_t)(row * a.ldw * 2 + ld_c * 16);
-    x_voff[j] = (uint32_t)(row * a.ldx * 2 + ld_c * 16);
-    st_off[j] = lds_off(row, ld_c);
-  }
+  const uint32_t w_voff = (uint32_t)(ld_row * a.ldw * 2 + ld_c * 16);
+  const uint32_t x_voff = (uint32_t)(ld_row * a.ldx * 2 + ld_c * 16);
+  const uint32_t w_rowstep = (uint32_t)(32 * a.ldw * 2), x_rowstep = (uint32_t)(32 * a.ldx * 2);
+  // rows j*32 + ld_row share row & 15, so the fill offset of chunk j is st_off + j * 4096
+  const uint32_t st_off = lds_off(ld_row, ld_c);
 
-  u32x4 wreg[8], xreg[8];
-  auto load_step = [&](int k0) {
-    const bool k_ok = k0 + ld_c * 8 < K;  // K is a multiple of 8: a chunk is all-in or all-out
+  // One register stage set: chunks 0..7 of W then 0..7 of X. During step s, quarter q of
+  // the set (holding step s+1) is written to LDS buffer (s+1)&1, then the same registers
+  // receive quarter q of step s+2 — a full step of latency for every load.
+  u32x4 stage[16];
+
+  // MASKED: the step may end past K (only the last step can), so chunks at or beyond K
+  // read as zero; otherwise the whole step is inside K.
+  auto load_q = [&](int k0, int q, auto masked_c) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const bool k_ok = !MASKED || k0 + ld_c * 8 < K;  // K is a multiple of 8
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      wreg[j] = buffer_load_16B(rW, k_ok ? w_voff[j] + k0 * 2 : kOobOffset);
-      xreg[j] = buffer_load_16B(rX, k_ok ? x_voff[j] + k0 * 2 : kOobOffset);
+    for (int i = 0; i < 4; ++i) {
+      const int c = q * 4 + i;
+      const int j = c & 7;
+      uint32_t voff = (c < 8 ? w_voff : x_voff) + (uint32_t)k0 * 2;
+      if constexpr (MASKED) voff = k_ok ? voff : kOobOffset;
+      stage[c] = __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? rW : rX, voff,
+                                                       j * (c < 8 ? w_rowstep : x_rowstep), 0);
     }
   };
-  auto store_step = [&](int stage) {
-    uint8_t* wb = smem + stage * 2 * kTileBytes;
-    uint8_t* xb = wb + kTileBytes;
+  auto store_q = [&](int buf, int q) __attribute__((always_inline)) {
+    uint8_t* wb = smem + buf * (2 * kTileBytes) + st_off;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      *reinterpret_cast<u32x4*>(wb + st_off[j]) = wreg[j];
-      *reinterpret_cast<u32x4*>(xb + st_off[j]) = xreg[j];
+    for (int i = 0; i < 4; ++i) {
+      const int c = q * 4 + i;
+      *reinterpret_cast<u32x4*>(wb + (c < 8 ? 0 : kTileBytes) + (c & 7) * 4096) = stage[c];
     }
   };
 
@@ -117,46 +133,119 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   // Per-lane operand read offsets: row (lane % 32) of each 32-row block, logical chunk
-  // 2*kk + lane/32. Block bases are multiples of 8 rows, so the swizzle uses lane % 8.
+  // 2*kk + lane/32. Block bases are multiples of 32 rows, so the swizzle uses lane % 32.
   const int a_row0 = wf * 128 + (lane & 31);
   const int b_row0 = wt * 128 + (lane & 31);
   uint32_t koff[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) koff[kk] = (uint32_t)((((kk * 2 + (lane >> 5)) ^ (lane & 7))) << 4);
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = (uint32_t)((((kk * 2 + (lane >> 5)) ^ swz(lane & 31))) << 4);
 
-  const int steps = (K + BK - 1) / BK;
-  load_step(0);
-  store_step(0);
-  __syncthreads();
-
-  for (int s = 0; s < steps; ++s) {
-    if (s + 1 < steps) load_step((s + 1) * BK);
-    const uint8_t* wb = smem + (s & 1) * 2 * kTileBytes;
+  bf16x8 fa[2][4], fb_[2][4];
+  auto read_frags = [&](int buf, int kk, bf16x8 (&af)[4], bf16x8 (&bf)[4]) __attribute__((always_inline)) {
+    const uint8_t* wb = smem + buf * (2 * kTileBytes);
     const uint8_t* xb = wb + kTileBytes;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 af[4], bfr[4];
+    for (int f = 0; f < 4; ++f) af[f] = *reinterpret_cast<const bf16x8*>(wb + (a_row0 + f * 32) * 128 + koff[kk]);
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
-        af[fb] = *reinterpret_cast<const bf16x8*>(wb + (a_row0 + fb * 32) * 128 + koff[kk]);
+    for (int t = 0; t < 4; ++t) bf[t] = *reinterpret_cast<const bf16x8*>(xb + (b_row0 + t * 32) * 128 + koff[kk]);
+  };
+
+  // One K step s from LDS buffer s&1. WRITE: fill buffer (s+1)&1 from the stage set (data
+  // of the next step); LOAD: then reload the stage set with step s+2 (0 none, 1 full step,
+  // 2 a step that may end past K). The fragment reads of sub-step kk+1 and the fills /
+  // loads are interleaved with sub-step kk's MFMAs.
+  auto kstep = [&](auto write_c, auto load_c, int s) __attribute__((always_inline)) {
+    const int CUR = s & 1;
+    constexpr bool WRITE = decltype(write_c)::value;
+    constexpr int LOADK = decltype(load_c)::value;
+    constexpr bool LOAD = LOADK != 0;
+    read_frags(CUR, 0, fa[0], fb_[0]);
+    // sub-step kk is a compile-time constant so every register array index is static
+    auto sub = [&](auto kk_c) __attribute__((always_inline)) {
+      constexpr int kk = decltype(kk_c)::value;
+      // keep each sub-step's work together: at most one sub-step of fragments in flight
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kk < 3) read_frags(CUR, kk + 1, fa[(kk + 1) & 1], fb_[(kk + 1) & 1]);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        bfr[tb] = *reinterpret_cast<const bf16x8*>(xb + (b_row0 + tb * 32) * 128 + koff[kk]);
+      for (int f = 0; f < 4; ++f)
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
+        for (int t = 0; t < 4; ++t)
+          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][f], fb_[kk & 1][t], acc[f][t], 0, 0, 0);
+      if constexpr (WRITE) store_q(CUR ^ 1, kk);
+      if constexpr (LOADK == 1) load_q((s + 2) * BK, kk, std::false_type{});
+      if constexpr (LOADK == 2) load_q((s + 2) * BK, kk, std::true_type{});
+      // issue pattern per sub-step: MFMA / DS-read pairs, then MFMAs interleaved with the
+      // fills and the global loads
+      if constexpr (kk < 3) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-          acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fb], bfr[tb], acc[fb][tb], 0, 0, 0);
-    }
-    if (s + 1 < steps) store_step((s + 1) & 1);
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+      if constexpr (WRITE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+      }
+      if constexpr (LOAD) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+    };
+    sub(std::integral_constant<int, 0>{});
+    sub(std::integral_constant<int, 1>{});
+    sub(std::integral_constant<int, 2>{});
+    sub(std::integral_constant<int, 3>{});
     __syncthreads();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using L0 = std::integral_constant<int, 0>;   // no load
+  using LF = std::integral_constant<int, 1>;   // full-step load
+  using LM = std::integral_constant<int, 2>;   // masked (possibly last) step load
+
+  const int steps = (K + BK - 1) / BK;
+  // prologue: step 0 into LDS buffer 0, step 1 into the stage set
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load_q(0, q, T{});
+#pragma unroll
+  for (int q = 0; q < 4; ++q) store_q(0, q);
+  if (steps > 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_q(BK, q, T{});
+  }
+  __syncthreads();
+
+  // steady state: the loads issued here (step s+2 <= steps-2) never reach the last,
+  // possibly partial, step
+  int s = 0;
+#pragma clang loop unroll(disable)
+  for (; s + 4 <= steps; ++s) kstep(T{}, LF{}, s);
+  // tail: the last three steps (or fewer)
+  if (steps >= 3) {
+    kstep(T{}, LM{}, s);
+    kstep(T{}, L0{}, s + 1);
+    kstep(F{}, L0{}, s + 2);
+  } else if (steps == 2) {
+    kstep(T{}, L0{}, 0);
+    kstep(F{}, L0{}, 1);
+  } else {
+    kstep(F{}, L0{}, 0);
   }
 
   // Epilogue: the 256 x 256 fp32 tile is staged through LDS in two 128-token passes
   // (128 KB each); pass p takes the accumulators of the waves with wt == p.
   run_staged_epilogue<BF, 1, 128, 2>(
       a, reinterpret_cast<float*>(smem), t0, f0, min(BT, a.M - t0), tt, slot,
-      [&](int p, float* tile) {
+      [&](int p, float* tile) __attribute__((always_inline)) {
         if (wt != p) return;
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
