@@ -348,9 +348,12 @@ __device__ __forceinline__ void run_staged_epilogue(const GemmArgs& a, float* ti
                                                     StageFn&& stage) {
   const EpiParams& e = a.ep;
   const int rounds = e.quant ? 2 : 1;
+  // rolled loops: one inlined copy of the chain serves every round and pass
+#pragma clang loop unroll(disable)
   for (int round = 0; round < rounds; ++round) {
     if (round == 1) rendezvous_wait(e.ws, rb, a.tiles_f);
     const int mode = e.quant ? (round == 0 ? EPI_AMAX : EPI_QUANT) : EPI_STORE;
+#pragma clang loop unroll(disable)
     for (int p = 0; p < PASSES; ++p) {
       const int rows = min(ROWS, nrows_total - p * ROWS);
       if (rows <= 0) break;

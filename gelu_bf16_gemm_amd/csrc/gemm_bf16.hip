@@ -102,17 +102,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   // receive quarter q of step s+2 — a full step of latency for every load.
   u32x4 stage[16];
 
-  // MASKED: the step may end past K (only the last step can), so chunks at or beyond K
-  // read as zero; otherwise the whole step is inside K.
-  auto load_q = [&](int k0, int q, auto masked_c) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_c)::value;
-    const bool k_ok = !MASKED || k0 + ld_c * 8 < K;  // K is a multiple of 8
+  // Chunks at or past K read as zero: the high offset bit makes the access out of range
+  // (arithmetic rather than a select, so the loads stay branch-free).
+  auto load_q = [&](int k0, int q) __attribute__((always_inline)) {
+    const uint32_t oob = (uint32_t)(k0 + ld_c * 8 >= K) << 31;  // K is a multiple of 8
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = q * 4 + i;
       const int j = c & 7;
-      uint32_t voff = (c < 8 ? w_voff : x_voff) + (uint32_t)k0 * 2;
-      if constexpr (MASKED) voff = k_ok ? voff : kOobOffset;
+      const uint32_t voff = ((c < 8 ? w_voff : x_voff) + (uint32_t)k0 * 2) | oob;
       stage[c] = __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? rW : rX, voff,
                                                        j * (c < 8 ? w_rowstep : x_rowstep), 0);
     }
@@ -150,15 +148,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
     for (int t = 0; t < 4; ++t) bf[t] = *reinterpret_cast<const bf16x8*>(xb + (b_row0 + t * 32) * 128 + koff[kk]);
   };
 
-  // One K step s from LDS buffer s&1. WRITE: fill buffer (s+1)&1 from the stage set (data
-  // of the next step); LOAD: then reload the stage set with step s+2 (0 none, 1 full step,
-  // 2 a step that may end past K). The fragment reads of sub-step kk+1 and the fills /
-  // loads are interleaved with sub-step kk's MFMAs.
-  auto kstep = [&](auto write_c, auto load_c, int s) __attribute__((always_inline)) {
+  // One K step s from LDS buffer s&1: the MFMAs of the step, the fill of buffer (s+1)&1
+  // from the stage set (data of step s+1), and the loads of step s+2 into the stage set.
+  // The fragment reads of sub-step kk+1 and the fills / loads are interleaved with
+  // sub-step kk's MFMAs. The last two steps fill and load past the end of K: those loads
+  // read zeros into a buffer that is not read again.
+  auto kstep = [&](int s) __attribute__((always_inline)) {
     const int CUR = s & 1;
-    constexpr bool WRITE = decltype(write_c)::value;
-    constexpr int LOADK = decltype(load_c)::value;
-    constexpr bool LOAD = LOADK != 0;
     read_frags(CUR, 0, fa[0], fb_[0]);
     // sub-step kk is a compile-time constant so every register array index is static
     auto sub = [&](auto kk_c) __attribute__((always_inline)) {
@@ -171,9 +167,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][f], fb_[kk & 1][t], acc[f][t], 0, 0, 0);
-      if constexpr (WRITE) store_q(CUR ^ 1, kk);
-      if constexpr (LOADK == 1) load_q((s + 2) * BK, kk, std::false_type{});
-      if constexpr (LOADK == 2) load_q((s + 2) * BK, kk, std::true_type{});
+      store_q(CUR ^ 1, kk);
+      load_q((s + 2) * BK, kk);
       // issue pattern per sub-step: MFMA / DS-read pairs, then MFMAs interleaved with the
       // fills and the global loads
       if constexpr (kk < 3) {
@@ -185,19 +180,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
-      if constexpr (WRITE) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        }
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       }
-      if constexpr (LOAD) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     };
     sub(std::integral_constant<int, 0>{});
@@ -206,40 +197,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
     sub(std::integral_constant<int, 3>{});
     __syncthreads();
   };
-  using T = std::true_type;
-  using F = std::false_type;
-  using L0 = std::integral_constant<int, 0>;   // no load
-  using LF = std::integral_constant<int, 1>;   // full-step load
-  using LM = std::integral_constant<int, 2>;   // masked (possibly last) step load
 
   const int steps = (K + BK - 1) / BK;
   // prologue: step 0 into LDS buffer 0, step 1 into the stage set
 #pragma unroll
-  for (int q = 0; q < 4; ++q) load_q(0, q, T{});
+  for (int q = 0; q < 4; ++q) load_q(0, q);
 #pragma unroll
   for (int q = 0; q < 4; ++q) store_q(0, q);
-  if (steps > 1) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load_q(BK, q, T{});
-  }
+  for (int q = 0; q < 4; ++q) load_q(BK, q);
   __syncthreads();
 
-  // steady state: the loads issued here (step s+2 <= steps-2) never reach the last,
-  // possibly partial, step
-  int s = 0;
 #pragma clang loop unroll(disable)
-  for (; s + 4 <= steps; ++s) kstep(T{}, LF{}, s);
-  // tail: the last three steps (or fewer)
-  if (steps >= 3) {
-    kstep(T{}, LM{}, s);
-    kstep(T{}, L0{}, s + 1);
-    kstep(F{}, L0{}, s + 2);
-  } else if (steps == 2) {
-    kstep(T{}, L0{}, 0);
-    kstep(F{}, L0{}, 1);
-  } else {
-    kstep(F{}, L0{}, 0);
-  }
+  for (int s = 0; s < steps; ++s) kstep(s);
 
   // Epilogue: the 256 x 256 fp32 tile is staged through LDS in two 128-token passes
   // (128 KB each); pass p takes the accumulators of the waves with wt == p.
