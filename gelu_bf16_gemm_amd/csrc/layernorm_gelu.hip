@@ -3,12 +3,17 @@
 //
 // A row is read with 16-byte loads: chunk j of lane l is the 16 bytes at chunk index
 // j * (64 * WPR) + l, so every load instruction of a wave covers 1 KB of contiguous
-// memory. All of a lane's chunks are loaded before any arithmetic, the row sits in
-// registers as fp32, and the statistics take two wavefront reductions (mean, then
-// the sum of squared deviations from it, matching the two-pass definition). Rows of
-// up to 64 * CH * EPC elements use one wave (WPR = 1); longer rows use a whole
-// workgroup (WPR = 4) with an LDS merge of the four waves' sums. Chunks past the row
-// end are masked out of both sums.
+// memory. All of a lane's chunks are loaded before any arithmetic and the row stays in
+// registers. The statistics take two reductions (mean, then the sum of squared
+// deviations from it, matching the two-pass definition); each is a DPP reduction inside
+// 16-lane rows plus four lane reads, so no LDS round trips. Chunks past the row end are
+// masked out of both sums.
+//
+// Rows of up to 64 * CH * EPC elements use one wave per row in persistent workgroups
+// that stage gamma and beta in LDS once and then stream rows; longer rows use a whole
+// workgroup (WPR = 4) per row with an LDS merge of the four waves' sums.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -77,7 +82,7 @@ __device__ __forceinline__ void store_chunk(void* base, int dtype, int64_t idx, 
 
 template <int WPR>
 __device__ __forceinline__ float row_sum(float v, float* lds, int wave_in_row) {
-  v = wave_sum(v);
+  v = wave_sum_uniform(v);
   if constexpr (WPR > 1) {
     const int lane = threadIdx.x & 63;
     __syncthreads();
@@ -169,6 +174,242 @@ __global__ __launch_bounds__(kThreads) void ln_gelu_kernel(LnArgs a) {
   }
 }
 
+// x element i (of EPC) of a 16-byte chunk, as fp32
+template <int EPC>
+__device__ __forceinline__ float chunk_elem(const u32x4& v, int dtype, int i) {
+  if constexpr (EPC == 4) {
+    return __uint_as_float(v[i]);
+  } else {
+    const uint32_t w = v[i >> 1];
+    if (dtype == FUSEDOPS_BF16) return (i & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    return f16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xFFFF));
+  }
+}
+
+// One wave per row, persistent workgroups; gamma / beta staged in LDS in their own dtype.
+template <int CH, int EPC>
+__global__ __launch_bounds__(kThreads)
+void ln_gelu_rows_kernel(LnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t gb[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cols = a.cols;
+  const int nchunks = cols / EPC;
+  const int pb = a.param_dtype == FUSEDOPS_F32 ? 4 : 2;
+  const int pbytes = (cols * pb + 15) & ~15;
+  const bool has_g = a.gamma != nullptr, has_b = a.beta != nullptr;
+  for (int i = threadIdx.x; i < pbytes / 16; i += kThreads) {
+    if (has_g) *reinterpret_cast<u32x4*>(gb + i * 16) = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.gamma) + i * 16);
+    if (has_b) *reinterpret_cast<u32x4*>(gb + pbytes + i * 16) = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.beta) + i * 16);
+  }
+  __syncthreads();
+  const int xb = a.io_dtype == FUSEDOPS_F32 ? 4 : 2;
+  const int yb = a.out_dtype == FUSEDOPS_F32 ? 4 : 2;
+  const float inv_cols = 1.0f / (float)cols;
+
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < a.rows; row += (int64_t)gridDim.x * 4) {
+    const char* xrow = static_cast<const char*>(a.x) + row * a.ldx * xb;
+    u32x4 xr[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = j * 64 + lane;
+      xr[j] = c < nchunks ? *reinterpret_cast<const u32x4*>(xrow + (int64_t)c * 16) : u32x4{0, 0, 0, 0};
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) s += chunk_elem<EPC>(xr[j], a.io_dtype, i);
+    const float mean = wave_sum_uniform(s) * inv_cols;
+    // keep only the packed row live between passes (widening again is one instruction per
+    // element; keeping 64 widened values would halve the occupancy)
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("" : "+v"(xr[j]));
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (j * 64 + lane < nchunks) {
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) {
+          const float d = chunk_elem<EPC>(xr[j], a.io_dtype, i) - mean;
+          q += d * d;
+        }
+      }
+    }
+    const float var = wave_sum_uniform(q) * inv_cols;
+    const float rstd = 1.0f / sqrtf(var + a.eps);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("" : "+v"(xr[j]));
+
+    char* yrow = static_cast<char*>(a.y) + row * a.ldy * yb;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = j * 64 + lane;
+      __builtin_amdgcn_sched_barrier(0);  // one chunk's parameters at a time
+      if (c >= nchunks) continue;
+      float g[EPC], b[EPC];
+      if (has_g) {
+        load_chunk<EPC>(gb, a.param_dtype, (int64_t)c * EPC, g);
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) g[i] = 1.f;
+      }
+      if (has_b) {
+        load_chunk<EPC>(gb + pbytes, a.param_dtype, (int64_t)c * EPC, b);
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) b[i] = 0.f;
+      }
+      float o[EPC];
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        const float yv = (chunk_elem<EPC>(xr[j], a.io_dtype, i) - mean) * rstd * g[i] + b[i];
+        o[i] = a.gelu_form == FUSEDOPS_GELU_TANH ? gelu_tanh_f32(yv)
+               : a.gelu_form == FUSEDOPS_GELU_ERF ? gelu_erf_f32(yv) : yv;
+      }
+      store_chunk<EPC>(yrow, a.out_dtype, (int64_t)c * EPC, o);
+    }
+  }
+}
+
+// Fast path: x, y, gamma and beta all in the same 2-byte type DT, GELU form FORM fixed at
+// compile time, so the per-element code has no branches. Rows are read and written
+// through buffer resources sized to the row: a chunk past the row end reads as zero and
+// its store is dropped, so ragged rows need no masked branches either.
+template <int DT>
+__device__ __forceinline__ float wide(uint32_t w, int hi) {
+  if constexpr (DT == FUSEDOPS_BF16) return hi ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+  else return f16_bits_to_f32(hi ? (w >> 16) : (w & 0xFFFF));
+}
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float a, float b) {
+  if constexpr (DT == FUSEDOPS_BF16) return pack_bf16x2(a, b);
+  else return pack_f16x2(a, b);
+}
+template <int FORM>
+__device__ __forceinline__ float act(float v) {
+  if constexpr (FORM == FUSEDOPS_GELU_TANH) return gelu_tanh_f32(v);
+  else if constexpr (FORM == FUSEDOPS_GELU_ERF) return gelu_erf_f32(v);
+  else return v;
+}
+
+template <int CH, int DT, int FORM>
+__global__ __launch_bounds__(kThreads) void ln_gelu_fast_kernel(LnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t gb[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cols = a.cols;
+  const int nchunks = cols / 8;
+  const int pbytes = (cols * 2 + 15) & ~15;
+  const bool has_g = a.gamma != nullptr, has_b = a.beta != nullptr;
+  for (int i = threadIdx.x; i < pbytes / 16; i += kThreads) {
+    // 1.0 in bf16 is 0x3F80, in fp16 0x3C00
+    const uint32_t one2 = DT == FUSEDOPS_BF16 ? 0x3F803F80u : 0x3C003C00u;
+    *reinterpret_cast<u32x4*>(gb + i * 16) =
+        has_g ? *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.gamma) + i * 16) : u32x4{one2, one2, one2, one2};
+    *reinterpret_cast<u32x4*>(gb + pbytes + i * 16) =
+        has_b ? *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.beta) + i * 16) : u32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+  const float inv_cols = 1.0f / (float)cols;
+  const uint32_t row_bytes = (uint32_t)cols * 2;
+
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < a.rows; row += (int64_t)gridDim.x * 4) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const uint16_t*>(a.x) + row * a.ldx, row_bytes);
+    u32x4 xr[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) xr[j] = buffer_load_16B(rx, (uint32_t)(j * 64 + lane) * 16);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += wide<DT>(xr[j][i >> 1], i & 1);
+    const float mean = wave_sum_uniform(s) * inv_cols;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("" : "+v"(xr[j]));
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const float valid = (j * 64 + lane) < nchunks ? 1.f : 0.f;
+      float qj = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float d = wide<DT>(xr[j][i >> 1], i & 1) - mean;
+        qj += d * d;
+      }
+      q += valid * qj;
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum_uniform(q) * inv_cols + a.eps);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("" : "+v"(xr[j]));
+
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + row * a.ldy, row_bytes);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      __builtin_amdgcn_sched_barrier(0);  // one chunk's parameters at a time
+      const int c = j * 64 + lane;
+      const int cp = c < nchunks ? c : nchunks - 1;  // parameter chunk stays inside the arrays
+      const u32x4 gw = *reinterpret_cast<const u32x4*>(gb + cp * 16);
+      const u32x4 bw = *reinterpret_cast<const u32x4*>(gb + pbytes + cp * 16);
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y0 = (wide<DT>(xr[j][i], 0) - mean) * rstd * wide<DT>(gw[i], 0) + wide<DT>(bw[i], 0);
+        const float y1 = (wide<DT>(xr[j][i], 1) - mean) * rstd * wide<DT>(gw[i], 1) + wide<DT>(bw[i], 1);
+        o[i] = narrow2<DT>(act<FORM>(y0), act<FORM>(y1));
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(o, ry, (uint32_t)c * 16, 0, 0);
+    }
+  }
+}
+
+template <int CH, int DT, int FORM>
+hipError_t launch_fast(const LnArgs& a, hipStream_t stream) {
+  const size_t lds = 2 * (size_t)((a.cols * 2 + 15) & ~15);
+  const void* fn = reinterpret_cast<const void*>(&ln_gelu_fast_kernel<CH, DT, FORM>);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds);
+  if (e != hipSuccess) return e;
+  const int64_t need = (a.rows + 3) / 4;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(need, (int64_t)cus * std::max(per_cu, 1)));
+  LnArgs copy = a;
+  void* args[] = {&copy};
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);
+}
+
+template <int DT, int FORM>
+hipError_t dispatch_fast(const LnArgs& a, hipStream_t stream) {
+  const int chunks = a.cols / 8;
+  if (chunks <= 64) return launch_fast<1, DT, FORM>(a, stream);
+  if (chunks <= 128) return launch_fast<2, DT, FORM>(a, stream);
+  if (chunks <= 256) return launch_fast<4, DT, FORM>(a, stream);
+  return launch_fast<8, DT, FORM>(a, stream);
+}
+
+template <int DT>
+hipError_t dispatch_fast_form(const LnArgs& a, hipStream_t stream) {
+  if (a.gelu_form == FUSEDOPS_GELU_TANH) return dispatch_fast<DT, FUSEDOPS_GELU_TANH>(a, stream);
+  if (a.gelu_form == FUSEDOPS_GELU_ERF) return dispatch_fast<DT, FUSEDOPS_GELU_ERF>(a, stream);
+  return dispatch_fast<DT, FUSEDOPS_GELU_NONE>(a, stream);
+}
+
+template <int CH, int EPC>
+hipError_t launch_rows(const LnArgs& a, hipStream_t stream) {
+  const int pb = a.param_dtype == FUSEDOPS_F32 ? 4 : 2;
+  const size_t lds = 2 * (size_t)((a.cols * pb + 15) & ~15);
+  const void* fn = reinterpret_cast<const void*>(&ln_gelu_rows_kernel<CH, EPC>);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds);
+  if (e != hipSuccess) return e;
+  const int64_t need = (a.rows + 3) / 4;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(need, (int64_t)cus * std::max(per_cu, 1)));
+  LnArgs copy = a;
+  void* args[] = {&copy};
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);
+}
+
 template <int CH, int EPC, int WPR>
 hipError_t launch(const LnArgs& a, hipStream_t stream) {
   const int rows_per_block = 4 / WPR;
@@ -182,20 +423,26 @@ hipError_t launch(const LnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_layernorm_gelu(const LnArgs& a, hipStream_t stream) {
+  // one 2-byte type throughout and a row a single wave can hold: the branch-free path
+  const bool same2 = a.io_dtype != FUSEDOPS_F32 && a.out_dtype == a.io_dtype &&
+                     ((!a.gamma && !a.beta) || a.param_dtype == a.io_dtype);
+  if (same2 && a.cols <= 64 * 8 * 8) {
+    return a.io_dtype == FUSEDOPS_BF16 ? dispatch_fast_form<FUSEDOPS_BF16>(a, stream)
+                                       : dispatch_fast_form<FUSEDOPS_F16>(a, stream);
+  }
   if (a.io_dtype == FUSEDOPS_F32) {
     const int chunks = a.cols / 4;
-    if (chunks <= 64) return launch<1, 4, 1>(a, stream);
-    if (chunks <= 128) return launch<2, 4, 1>(a, stream);
-    if (chunks <= 256) return launch<4, 4, 1>(a, stream);
-    if (chunks <= 512) return launch<8, 4, 1>(a, stream);
-    if (chunks <= 1024) return launch<16, 4, 1>(a, stream);
+    if (chunks <= 64) return launch_rows<1, 4>(a, stream);
+    if (chunks <= 128) return launch_rows<2, 4>(a, stream);
+    if (chunks <= 256) return launch_rows<4, 4>(a, stream);
+    if (chunks <= 512) return launch_rows<8, 4>(a, stream);
     return launch<16, 4, 4>(a, stream);
   }
   const int chunks = a.cols / 8;
-  if (chunks <= 64) return launch<1, 8, 1>(a, stream);
-  if (chunks <= 128) return launch<2, 8, 1>(a, stream);
-  if (chunks <= 256) return launch<4, 8, 1>(a, stream);
-  if (chunks <= 512) return launch<8, 8, 1>(a, stream);
+  if (chunks <= 64) return launch_rows<1, 8>(a, stream);
+  if (chunks <= 128) return launch_rows<2, 8>(a, stream);
+  if (chunks <= 256) return launch_rows<4, 8>(a, stream);
+  if (chunks <= 512) return launch_rows<8, 8>(a, stream);
   return launch<8, 8, 4>(a, stream);
 }
 
