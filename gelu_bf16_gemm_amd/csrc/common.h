@@ -25,6 +25,10 @@ constexpr int kWave = 64;
 constexpr int kBufferRsrcWord3 = 0x00020000;
 // A voffset that is always out of range, so the buffer load returns zero.
 constexpr uint32_t kOobOffset = 0x80000000u;
+// Cache-policy operand of a buffer access asking for nontemporal (streaming) treatment:
+// the `nt` bit on gfx94x / gfx950. Data read exactly once should not displace data
+// that is reused.
+constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -54,12 +58,15 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// Two fp32 -> two bf16 packed (low half = a).
+// Two fp32 -> two bf16 / fp16 packed (low half = a), one v_cvt_pk_{bf16,f16}_f32 each
+// (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, v2{(__bf16)a, (__bf16)b});
 }
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  return f32_to_f16_bits(a) | (f32_to_f16_bits(b) << 16);
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, v2{(_Float16)a, (_Float16)b});
 }
 
 // Two fp32 -> two OCP E4M3 codes (low byte = a); inputs must already be clamped to +-448.
@@ -143,14 +150,20 @@ __device__ __forceinline__ float gelu_erf_f32(float v) {
 }
 
 // GELU, tanh form. 0.5 v (1 + tanh u) equals v / (1 + e^{-2u}), which needs one exp
-// and one reciprocal; u = sqrt(2/pi) (v + 0.044715 v^3).
+// and one reciprocal; u = sqrt(2/pi) (v + 0.044715 v^3). The constants -2 sqrt(2/pi) and
+// log2(e) are folded so that e^{-2u} = 2^{v (A + B v^2)} with
+// A = -2 sqrt(2/pi) log2(e) and B = 0.044715 A: three VALU ops and one v_exp_f32.
 __device__ __forceinline__ float gelu_tanh_f32(float v) {
-  const float u = 0.79788456080286536f * (v + 0.044715f * v * v * v);
-  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+  constexpr double kA = -2.0 * 0.79788456080286536 * 1.4426950408889634;
+  constexpr float A = (float)kA, B = (float)(kA * 0.044715);
+  const float t = v * __builtin_fmaf(v * v, B, A);
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
-// silu(g) = g / (1 + e^-g).
-__device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g) = g / (1 + 2^{-g log2 e}).
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
 
 // ---------------------------------------------------------------------------
 // wave reductions

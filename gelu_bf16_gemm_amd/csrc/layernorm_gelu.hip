@@ -100,7 +100,7 @@ template <int CH, int EPC, int WPR>
 __global__ __launch_bounds__(kThreads) void ln_gelu_kernel(LnArgs a) {
   __shared__ float lds[4];
   constexpr int kRowsPerBlock = 4 / WPR;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row_in_block = wave / WPR, wave_in_row = wave % WPR;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + row_in_block;
   // WPR > 1 has one row per block, so `row < rows` is uniform across the block's barriers.
@@ -191,7 +191,7 @@ template <int CH, int EPC>
 __global__ __launch_bounds__(kThreads)
 void ln_gelu_rows_kernel(LnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t gb[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int cols = a.cols;
   const int nchunks = cols / EPC;
   const int pb = a.param_dtype == FUSEDOPS_F32 ? 4 : 2;
@@ -285,6 +285,16 @@ __device__ __forceinline__ uint32_t narrow2(float a, float b) {
   if constexpr (DT == FUSEDOPS_BF16) return pack_bf16x2(a, b);
   else return pack_f16x2(a, b);
 }
+template <int DT>
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+  if constexpr (DT == FUSEDOPS_BF16) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), bf16x2_t{1, 1}, acc, false);
+  } else {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), f16x2_t{1, 1}, acc, false);
+  }
+}
 template <int FORM>
 __device__ __forceinline__ float act(float v) {
   if constexpr (FORM == FUSEDOPS_GELU_TANH) return gelu_tanh_f32(v);
@@ -295,7 +305,7 @@ __device__ __forceinline__ float act(float v) {
 template <int CH, int DT, int FORM>
 __global__ __launch_bounds__(kThreads) void ln_gelu_fast_kernel(LnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t gb[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int cols = a.cols;
   const int nchunks = cols / 8;
   const int pbytes = (cols * 2 + 15) & ~15;
@@ -316,12 +326,14 @@ __global__ __launch_bounds__(kThreads) void ln_gelu_fast_kernel(LnArgs a) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const uint16_t*>(a.x) + row * a.ldx, row_bytes);
     u32x4 xr[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) xr[j] = buffer_load_16B(rx, (uint32_t)(j * 64 + lane) * 16);
+    for (int j = 0; j < CH; ++j)
+      xr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(j * 64 + lane) * 16, 0, kNonTemporal));
+    // row sum: one v_dot2 against (1, 1) adds a packed pair exactly into the fp32 total
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < CH; ++j)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s += wide<DT>(xr[j][i >> 1], i & 1);
+      for (int i = 0; i < 4; ++i) s = add_pair<DT>(xr[j][i], s);
     const float mean = wave_sum_uniform(s) * inv_cols;
 #pragma unroll
     for (int j = 0; j < CH; ++j) asm volatile("" : "+v"(xr[j]));
@@ -338,6 +350,7 @@ __global__ __launch_bounds__(kThreads) void ln_gelu_fast_kernel(LnArgs a) {
       q += valid * qj;
     }
     const float rstd = 1.0f / sqrtf(wave_sum_uniform(q) * inv_cols + a.eps);
+    const float shift = -mean * rstd;  // (x - mean) rstd = fma(x, rstd, shift)
 #pragma unroll
     for (int j = 0; j < CH; ++j) asm volatile("" : "+v"(xr[j]));
 
@@ -352,8 +365,10 @@ __global__ __launch_bounds__(kThreads) void ln_gelu_fast_kernel(LnArgs a) {
       u32x4 o;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float y0 = (wide<DT>(xr[j][i], 0) - mean) * rstd * wide<DT>(gw[i], 0) + wide<DT>(bw[i], 0);
-        const float y1 = (wide<DT>(xr[j][i], 1) - mean) * rstd * wide<DT>(gw[i], 1) + wide<DT>(bw[i], 1);
+        const float n0 = __builtin_fmaf(wide<DT>(xr[j][i], 0), rstd, shift);
+        const float n1 = __builtin_fmaf(wide<DT>(xr[j][i], 1), rstd, shift);
+        const float y0 = __builtin_fmaf(n0, wide<DT>(gw[i], 0), wide<DT>(bw[i], 0));
+        const float y1 = __builtin_fmaf(n1, wide<DT>(gw[i], 1), wide<DT>(bw[i], 1));
         o[i] = narrow2<DT>(act<FORM>(y0), act<FORM>(y1));
       }
       __builtin_amdgcn_raw_buffer_store_b128(o, ry, (uint32_t)c * 16, 0, 0);
@@ -361,17 +376,13 @@ __global__ __launch_bounds__(kThreads) void ln_gelu_fast_kernel(LnArgs a) {
   }
 }
 
+// One row per wave and four rows per block: the hardware dispatcher hands out rows as
+// blocks finish, which balances better than a persistent grid striding over rows.
 template <int CH, int DT, int FORM>
 hipError_t launch_fast(const LnArgs& a, hipStream_t stream) {
   const size_t lds = 2 * (size_t)((a.cols * 2 + 15) & ~15);
   const void* fn = reinterpret_cast<const void*>(&ln_gelu_fast_kernel<CH, DT, FORM>);
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds);
-  if (e != hipSuccess) return e;
-  const int64_t need = (a.rows + 3) / 4;
-  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(need, (int64_t)cus * std::max(per_cu, 1)));
+  const int64_t grid = (a.rows + 3) / 4;
   LnArgs copy = a;
   void* args[] = {&copy};
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, lds, stream);
@@ -383,6 +394,7 @@ hipError_t dispatch_fast(const LnArgs& a, hipStream_t stream) {
   if (chunks <= 64) return launch_fast<1, DT, FORM>(a, stream);
   if (chunks <= 128) return launch_fast<2, DT, FORM>(a, stream);
   if (chunks <= 256) return launch_fast<4, DT, FORM>(a, stream);
+  if (chunks <= 384) return launch_fast<6, DT, FORM>(a, stream);
   return launch_fast<8, DT, FORM>(a, stream);
 }
 

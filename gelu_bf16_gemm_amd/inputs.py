@@ -32,9 +32,14 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     Inputs are finite random draws, so NaN handling is not needed here.
     """
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = a.view(np.uint32)
+    # u + 0x7FFF + lsb stays below 2**32 for every finite float32 bit pattern
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
