@@ -19,8 +19,10 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -110,6 +112,45 @@ def cpu_baseline(seconds_target: float = 10.0, seconds_cap: float = 30.0) -> dic
                       f"{block}-row blocks; bias + GELU erf, fp64), {t_total:.1f} s of oracle time"}
 
 
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from its committed rocprofv3 summary
+    (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), or None when there is no
+    summary or the kernel's sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if m is None:
+        return None
+    rec = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for p in rec["sources"]:
+        h.update(p.encode())
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
+def copy_calibration(launches: int) -> dict:
+    """torch.neg over 1 GiB of fp32 into a second 1 GiB buffer: each launch reads and writes
+    exactly 2**30 bytes, the known size a profiler's HBM byte counters are divided by."""
+    import torch
+
+    n = 1 << 28
+    x = torch.empty(n, dtype=torch.float32, device="cuda").uniform_()
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(launches):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / launches
+    del x, y
+    torch.cuda.empty_cache()
+    return {"kernel": "torch.neg fp32 elementwise", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+            "launches": launches, "ms": round(ms, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +158,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None, help="comma-separated workload names (default: whole suite)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first stream 1 GiB through a plain elementwise kernel (read once, write once) "
+                         "so that HBM byte counters can be scaled against a known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -133,6 +177,7 @@ def main() -> int:
     names = [n for n, _ in SUITE] if args.only is None else args.only.split(",")
     bound = dict(SUITE)
     results = {}
+    calib = copy_calibration(args.steps) if args.copy_calibration else None
     for name in names:
         spec = I.WORKLOADS[name]
         print(f"[bench] {name}: inputs", file=sys.stderr, flush=True)
@@ -148,6 +193,7 @@ def main() -> int:
             r["TFLOP/s"] = round(fl / ms / 1e9, 2)
             peak = PEAK_F32_TFLOPS if spec.get("in_dtype") == I.F32 else PEAK_BF16_TFLOPS
             r["mfma_frac"] = round(fl / ms / 1e9 / peak, 4)
+        r["bytes"] = int(by)
         r["GB/s"] = round(by / ms / 1e6, 1)
         r["hbm_frac"] = round(by / ms / 1e6 / PEAK_HBM_GBPS, 4)
         results[name] = r
@@ -165,7 +211,9 @@ def main() -> int:
     if DOMINANT in results:
         d = results[DOMINANT]
         roof = {"bound": "mfma", "achieved": d["TFLOP/s"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(d["TFLOP/s"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(d["TFLOP/s"] / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic("gemm_bf16_t256_kernel", DOMINANT),
+                "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": int(d["bytes"]),
                 "kernel": "gemm_bf16_t256_kernel", "workload": DOMINANT}
     ln = results.get("ln_gelu_f16_32768x4096")
     line = {
@@ -175,10 +223,15 @@ def main() -> int:
         "config": {"workload": "fused-linear hot path suite (one pass of every workload at full size)",
                    "workloads": names},
         "roofline": roof,
-        "ln_gelu": None if ln is None else {"value": ln["GB/s"], "unit": "GB/s", "peak": PEAK_HBM_GBPS,
-                                            "frac": ln["hbm_frac"], "workload": "ln_gelu_f16_32768x4096"},
+        "ln_gelu": None if ln is None else {
+            "bound": "hbm", "achieved": ln["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ln["hbm_frac"],
+            "traffic": measured_traffic("ln_gelu_fast_kernel", "ln_gelu_f16_32768x4096"),
+            "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": int(ln["bytes"]),
+            "kernel": "ln_gelu_fast_kernel", "workload": "ln_gelu_f16_32768x4096"},
         "workloads": results,
     }
+    if calib is not None:
+        line["copy_calibration"] = calib
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline()
