@@ -1,0 +1,429 @@
+// Epilogue of the 256 x 256 bf16 tile kernel, run on the MFMA accumulators in place.
+//
+// The tile is computed transposed, D[f][t] = sum_k W[f][k] X[t][k]. Wave (wf, wt) of the
+// workgroup holds features wf*128 .. +127 and tokens wt*128 .. +127 of the tile as
+// acc[fb][tb] (4 x 4 blocks of v_mfma_f32_32x32x16_bf16 output). Register r of block
+// (fb, tb) in lane l holds
+//     local feature  wf*128 + fb*32 + 8*(r / 4) + 4*(l / 32) + (r % 4)
+//     local token    wt*128 + tb*32 + (l % 32)
+// so each lane owns runs ("groups") of four consecutive features of four tokens: 16 groups
+// (fb, q = r / 4) per token. This is the layout the chain runs in ([Epilogue] §模式A,
+// §模式B, §仿射量化与尾声的五步; op order as in the row-layout epilogue):
+//   * per-feature vectors (bias, column scale) are 16 four-wide loads per lane, once;
+//   * SwiGLU pairs (2j, 2j+1) lie in one group, so gate and up meet in the same lane;
+//   * a token's sum of squares over the wave's 128 features (one RMSNorm partial chunk)
+//     is an in-lane sum over 64 registers plus one exchange with lane l ^ 32; the FP8
+//     row absmax is reduced the same way;
+//   * only finished values cross LDS: they are written in the output storage type into a
+//     token-major, XOR-swizzled LDS tile, and the workgroup then stores whole rows with
+//     16-byte coalesced writes (plain, or split across up to three destinations).
+// Residual rows come in the other direction: a coalesced copy into the same LDS tile
+// layout, then per-group reads.
+#pragma once
+
+#include "epilogue.h"
+
+namespace fusedops {
+
+namespace epi {
+
+// Compile-time description of a kernel instance's epilogue. With kStatic set, the op set,
+// activation and storage types are fixed at compile time; otherwise every choice is read
+// from EpiParams at run time (the generic instance).
+constexpr uint32_t kStatic = 1u << 31;
+constexpr uint32_t kBias = 1u << 0, kZ = 1u << 1, kAux = 1u << 2, kPart = 1u << 3, kGamma = 1u << 4,
+                   kRscale = 1u << 5, kQuant = 1u << 6, kSplit = 1u << 7;
+constexpr int kActShift = 8, kYShift = 10, kZShift = 12, kAuxShift = 14, kBiasShift = 16, kGammaShift = 18;
+
+constexpr uint32_t config(uint32_t ops, int act, int y_dtype, int z_dtype = FUSEDOPS_BF16,
+                          int aux_dtype = FUSEDOPS_BF16, int bias_dtype = FUSEDOPS_BF16,
+                          int gamma_dtype = FUSEDOPS_BF16) {
+  return kStatic | ops | ((uint32_t)act << kActShift) | ((uint32_t)y_dtype << kYShift) |
+         ((uint32_t)z_dtype << kZShift) | ((uint32_t)aux_dtype << kAuxShift) |
+         ((uint32_t)bias_dtype << kBiasShift) | ((uint32_t)gamma_dtype << kGammaShift);
+}
+
+// The configuration a call's parameters describe (always with kStatic set).
+__host__ __device__ inline uint32_t config_of(const EpiParams& e) {
+  uint32_t ops = 0;
+  if (e.bias) ops |= kBias;
+  if (e.z) ops |= kZ;
+  if (e.aux) ops |= kAux;
+  if (e.partials) ops |= kPart;
+  if (e.gamma) ops |= kGamma;
+  if (e.rscale) ops |= kRscale;
+  if (e.quant) ops |= kQuant;
+  if (e.n_split) ops |= kSplit;
+  return config(ops, e.act, e.y_dtype, e.z ? e.z_dtype : FUSEDOPS_BF16, e.aux ? e.aux_dtype : FUSEDOPS_BF16,
+                e.bias ? e.bias_dtype : FUSEDOPS_BF16, e.gamma ? e.gamma_dtype : FUSEDOPS_BF16);
+}
+
+template <uint32_t F>
+struct Cfg {
+  static constexpr bool S = (F & kStatic) != 0;
+  const EpiParams& e;
+  __device__ bool bias() const { if constexpr (S) return F & kBias; else return e.bias != nullptr; }
+  __device__ bool z() const { if constexpr (S) return F & kZ; else return e.z != nullptr; }
+  __device__ bool aux() const { if constexpr (S) return F & kAux; else return e.aux != nullptr; }
+  __device__ bool part() const { if constexpr (S) return F & kPart; else return e.partials != nullptr; }
+  __device__ bool gamma() const { if constexpr (S) return F & kGamma; else return e.gamma != nullptr; }
+  __device__ bool rscale() const { if constexpr (S) return F & kRscale; else return e.rscale != nullptr; }
+  __device__ bool quant() const { if constexpr (S) return F & kQuant; else return e.quant != 0; }
+  __device__ bool split() const { if constexpr (S) return F & kSplit; else return e.n_split != 0; }
+  __device__ int act() const { if constexpr (S) return (F >> kActShift) & 3; else return e.act; }
+  __device__ int y_dt() const { if constexpr (S) return (F >> kYShift) & 3; else return e.y_dtype; }
+  __device__ int z_dt() const { if constexpr (S) return (F >> kZShift) & 3; else return e.z_dtype; }
+  __device__ int aux_dt() const { if constexpr (S) return (F >> kAuxShift) & 3; else return e.aux_dtype; }
+  __device__ int bias_dt() const { if constexpr (S) return (F >> kBiasShift) & 3; else return e.bias_dtype; }
+  __device__ int gamma_dt() const { if constexpr (S) return (F >> kGammaShift) & 3; else return e.gamma_dtype; }
+};
+
+}  // namespace epi
+
+namespace accepi {
+
+constexpr int kTileRows = 256;           // tokens per tile
+constexpr int kTileCols = 256;           // features per tile
+constexpr int kStageBytes = 128 * 1024;  // LDS available for one staged tile
+
+__device__ __forceinline__ int dt_bytes(int dt) {
+  return dt == FUSEDOPS_F32 ? 4 : (dt == FUSEDOPS_F8E4M3 ? 1 : 2);
+}
+
+// Byte offset of byte b of row r in a staged tile of C 16-byte chunks per row (C a power of
+// two): chunk c sits at position c ^ (r mod min(C, 32)). Rows of one group write are 32
+// consecutive tokens at one column, so those land on distinct chunk positions; row-wise
+// copies touch all positions of a row.
+__device__ __forceinline__ uint32_t st_off(int r, int b, int C) {
+  const int m = (C < 32 ? C : 32) - 1;
+  return (uint32_t)(r * C * 16 + ((((b >> 4) ^ (r & m))) << 4) + (b & 15));
+}
+
+// Write n = 4 (or 2) values of storage type dt at LDS byte offset off.
+__device__ __forceinline__ void lds_put(uint8_t* lds, uint32_t off, int dt, f32x4 v, int n) {
+  if (dt == FUSEDOPS_F32) {
+    if (n == 4) *reinterpret_cast<f32x4*>(lds + off) = v;
+    else *reinterpret_cast<float2*>(lds + off) = make_float2(v[0], v[1]);
+  } else if (dt == FUSEDOPS_F8E4M3) {
+    if (n == 4) *reinterpret_cast<uint32_t*>(lds + off) = pack_e4m3x2(v[0], v[1]) | (pack_e4m3x2(v[2], v[3]) << 16);
+    else *reinterpret_cast<uint16_t*>(lds + off) = (uint16_t)pack_e4m3x2(v[0], v[1]);
+  } else {
+    const bool bf = dt == FUSEDOPS_BF16;
+    const uint32_t lo = bf ? pack_bf16x2(v[0], v[1]) : pack_f16x2(v[0], v[1]);
+    if (n == 4) {
+      const uint32_t hi = bf ? pack_bf16x2(v[2], v[3]) : pack_f16x2(v[2], v[3]);
+      *reinterpret_cast<u32x2*>(lds + off) = u32x2{lo, hi};
+    } else {
+      *reinterpret_cast<uint32_t*>(lds + off) = lo;
+    }
+  }
+}
+
+// Read 4 values of storage type dt (bf16 / fp16 / fp32) at LDS byte offset off.
+__device__ __forceinline__ f32x4 lds_get4(const uint8_t* lds, uint32_t off, int dt) {
+  if (dt == FUSEDOPS_F32) return *reinterpret_cast<const f32x4*>(lds + off);
+  const u32x2 w = *reinterpret_cast<const u32x2*>(lds + off);
+  if (dt == FUSEDOPS_BF16)
+    return f32x4{bf16_bits_to_f32(w[0] & 0xFFFF), bf16_bits_to_f32(w[0] >> 16), bf16_bits_to_f32(w[1] & 0xFFFF),
+                 bf16_bits_to_f32(w[1] >> 16)};
+  return f32x4{f16_bits_to_f32(w[0] & 0xFFFF), f16_bits_to_f32(w[0] >> 16), f16_bits_to_f32(w[1] & 0xFFFF),
+               f16_bits_to_f32(w[1] >> 16)};
+}
+
+// Four consecutive elements of a feature vector (bias, column scale) as fp32, or `fill`
+// past the N features.
+__device__ __forceinline__ f32x4 vec4(const void* p, int dt, int f, int N, float fill) {
+  if (f >= N) return f32x4{fill, fill, fill, fill};
+  return load4(p, dt, f);
+}
+
+// Where a staged tile's rows go in global memory.
+struct Dest {
+  uint8_t* base[3];  // destination(s); more than one for a split store
+  int64_t ld;        // elements per row
+  int64_t split_w;   // columns per destination (0: a single destination)
+  int es;            // bytes per element
+  int cols;          // valid columns of the whole output (N, or N/2 after SwiGLU)
+  int col0;          // first output column of the tile
+};
+
+// Copy a staged tile (R rows of C chunks) to global memory: thread tid takes chunks
+// tid, tid + 256, ...; a chunk is one 16-byte store when it lies wholly inside the output
+// and one destination, otherwise 4-byte stores of its valid words.
+__device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int row0, int M, const Dest& d) {
+  const int cshift = __builtin_ctz(C);
+  for (int id = threadIdx.x; id < R * C; id += kEpiThreads) {
+    const int r = id >> cshift, c = id & (C - 1);
+    const int t = row0 + r;
+    if (t >= M) continue;
+    const int col = d.col0 + c * 16 / d.es;
+    if (col >= d.cols) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + st_off(r, c * 16, C));
+    const int per = 16 / d.es;  // elements per chunk
+    const int seg = d.split_w ? (int)(col / d.split_w) : 0;
+    const int64_t cseg = col - (int64_t)seg * d.split_w;
+    const bool whole = col + per <= d.cols && (!d.split_w || cseg + per <= d.split_w);
+    if (whole) {
+      *reinterpret_cast<u32x4*>(d.base[seg] + ((int64_t)t * d.ld + cseg) * d.es) = v;
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int cw = col + w * 4 / d.es;  // first column of word w
+        if (cw >= d.cols) break;
+        const int sw = d.split_w ? (int)(cw / d.split_w) : 0;
+        const int64_t cc = cw - (int64_t)sw * d.split_w;
+        *reinterpret_cast<uint32_t*>(d.base[sw] + ((int64_t)t * d.ld + cc) * d.es) = v[w];
+      }
+    }
+  }
+}
+
+}  // namespace accepi
+
+// Run the whole epilogue of one 256 x 256 tile whose accumulators are in `acc` (the
+// layout above). `lds` is at least 128 KB of LDS that the mainloop no longer uses; every
+// thread of the workgroup must call this.
+template <uint32_t F>
+__device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, int t0, int f0,
+                                             int rb, int* slot) {
+  using namespace accepi;
+  const EpiParams& e = a.ep;
+  const epi::Cfg<F> cfg{e};
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wf = wave >> 1, wt = wave & 1;
+  const int hb = lane >> 5, tl = lane & 31;
+  const int M = a.M, N = a.N;
+  // local feature of group (fb, q) and local token of block row tb
+  auto fl = [&](int fb, int q) { return wf * 128 + fb * 32 + q * 8 + hb * 4; };
+  auto tk = [&](int tb) { return wt * 128 + tb * 32 + tl; };
+
+  const int act = cfg.act();
+  const bool pairs = act == ACT_SWIGLU;
+  const bool fused = !cfg.z() && !cfg.aux() && !cfg.part() && !cfg.quant();
+
+  // Stage the lane's values (4 per group, or the 2 SwiGLU outputs per group) in storage
+  // type dt and store the tile to `d`. `val(fb, tb)` yields block (fb, tb); tiles larger
+  // than 128 KB go in two passes of 128 tokens, each staged by the waves that own them.
+  auto emit = [&](int dt, bool pr, const accepi::Dest& d, auto&& val) __attribute__((always_inline)) {
+    const int es = dt_bytes(dt);
+    const int cols = pr ? kTileCols / 2 : kTileCols;
+    const int C = cols * es / 16;
+    const int passes = kTileRows * cols * es > kStageBytes ? 2 : 1;
+    const int R = kTileRows / passes;
+#pragma clang loop unroll(disable)
+    for (int p = 0; p < passes; ++p) {
+      __syncthreads();
+      if (passes == 1 || wt == p) {
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            const f32x16 v = val(fb, tb);
+            const int r = tk(tb) - p * R;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 g{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+              if (pr) lds_put(lds, st_off(r, fl(fb, q) / 2 * es, C), dt, g, 2);
+              else lds_put(lds, st_off(r, fl(fb, q) * es, C), dt, g, 4);
+            }
+          }
+      }
+      __syncthreads();
+      copy_out(lds, R, C, t0 + p * R, M, d);
+    }
+  };
+
+  // per-feature vectors of feature block fb (16 values per lane)
+  auto feat = [&](const void* ptr, int dt, int fb, float fill) __attribute__((always_inline)) {
+    f32x16 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 x = vec4(ptr, dt, f0 + fl(fb, q), N, fill);
+      o[4 * q] = x[0]; o[4 * q + 1] = x[1]; o[4 * q + 2] = x[2]; o[4 * q + 3] = x[3];
+    }
+    return o;
+  };
+  auto rs_of = [&](int tb) __attribute__((always_inline)) {
+    const int t = t0 + tk(tb);
+    return t < M ? e.rscale[t] : 0.f;
+  };
+  // column scale, row scale, activation on one block (SwiGLU leaves the two outputs of
+  // group q in registers 4q and 4q + 1, zeros in 4q + 2 and 4q + 3)
+  auto post = [&](f32x16 v, const f32x16& g, int tb) __attribute__((always_inline)) {
+    if (cfg.gamma()) v *= g;
+    if (cfg.rscale()) v *= rs_of(tb);
+    if (act == ACT_GELU_ERF) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = gelu_erf_f32(v[r]);
+    } else if (act == ACT_GELU_TANH) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = gelu_tanh_f32(v[r]);
+    } else if (pairs) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float o0 = silu_f32(v[4 * q]) * v[4 * q + 1];
+        const float o1 = silu_f32(v[4 * q + 2]) * v[4 * q + 3];
+        v[4 * q] = o0; v[4 * q + 1] = o1; v[4 * q + 2] = 0.f; v[4 * q + 3] = 0.f;
+      }
+    }
+    return v;
+  };
+
+  const int ydt = cfg.y_dt();
+  accepi::Dest dy;
+  dy.es = dt_bytes(ydt);
+  dy.cols = pairs ? N / 2 : N;
+  dy.col0 = pairs ? f0 / 2 : f0;
+  if (cfg.split()) {
+    dy.base[0] = static_cast<uint8_t*>(e.yv0);
+    dy.base[1] = static_cast<uint8_t*>(e.yv1);
+    dy.base[2] = static_cast<uint8_t*>(e.yv2);
+    dy.ld = e.ldv;
+    dy.split_w = e.split_w;
+  } else {
+    dy.base[0] = static_cast<uint8_t*>(e.y);
+    dy.base[1] = dy.base[2] = nullptr;
+    dy.ld = e.ldy;
+    dy.split_w = 0;
+  }
+
+  if (fused) {
+    // bias, scales and activation straight into the staged output tile
+    f32x16 b = {}, g = {};
+    int fb_loaded = -1;
+    emit(ydt, pairs, dy, [&](int fb, int tb) __attribute__((always_inline)) {
+      if (fb != fb_loaded) {
+        if (cfg.bias()) b = feat(e.bias, cfg.bias_dt(), fb, 0.f);
+        if (cfg.gamma()) g = feat(e.gamma, cfg.gamma_dt(), fb, 1.f);
+        fb_loaded = fb;
+      }
+      f32x16 v = acc[fb][tb];
+      if (cfg.bias()) v += b;
+      return post(v, g, tb);
+    });
+    return;
+  }
+
+  // ---- pre-activation h1 = acc + bias + residual, in place
+  if (cfg.bias()) {
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      const f32x16 b = feat(e.bias, cfg.bias_dt(), fb, 0.f);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[fb][tb] += b;
+    }
+  }
+  if (cfg.z()) {
+    // coalesced copy of the residual rows into the staged-tile layout, then per-group reads;
+    // rows past M and columns past N read as zero
+    const int zdt = cfg.z_dt();
+    const int es = dt_bytes(zdt);
+    const int C = kTileCols * es / 16;
+    const int passes = kTileRows * kTileCols * es > kStageBytes ? 2 : 1;
+    const int R = kTileRows / passes;
+    const int cshift = __builtin_ctz(C);
+#pragma clang loop unroll(disable)
+    for (int p = 0; p < passes; ++p) {
+      __syncthreads();
+      for (int id = threadIdx.x; id < R * C; id += kEpiThreads) {
+        const int r = id >> cshift, c = id & (C - 1);
+        const int t = t0 + p * R + r;
+        const int col = f0 + c * 16 / es;
+        u32x4 v = u32x4{0, 0, 0, 0};
+        if (t < M && col < N)
+          v = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(e.z) + ((int64_t)t * e.ldz + col) * es);
+        *reinterpret_cast<u32x4*>(lds + st_off(r, c * 16, C)) = v;
+      }
+      __syncthreads();
+      if (passes == 1 || wt == p) {
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            f32x16 v = acc[fb][tb];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 z = lds_get4(lds, st_off(tk(tb) - p * R, fl(fb, q) * es, C), zdt);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) v[4 * q + j] += z[j];
+            }
+            acc[fb][tb] = v;
+          }
+      }
+    }
+  }
+  if (cfg.aux()) {
+    accepi::Dest d{{static_cast<uint8_t*>(e.aux), nullptr, nullptr}, e.ld_aux, 0, dt_bytes(cfg.aux_dt()), N, f0};
+    emit(cfg.aux_dt(), false, d, [&](int fb, int tb) __attribute__((always_inline)) { return acc[fb][tb]; });
+  }
+  if (cfg.part()) {
+    // sum of squares of the token's 128 features of this wave: one RMSNorm partial chunk
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      float s = 0.f;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s = __builtin_fmaf(acc[fb][tb][r], acc[fb][tb][r], s);
+      s += __shfl_xor(s, 32, kWave);
+      const int t = t0 + tk(tb);
+      if (hb == 0 && t < M && f0 + wf * 128 < N) e.partials[(int64_t)t * e.ldp + f0 / 128 + wf] = s;
+    }
+  }
+
+  // ---- column scale, row scale, activation, in place
+  if (cfg.gamma() || cfg.rscale() || act != ACT_NONE) {
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      f32x16 g = {};
+      if (cfg.gamma()) g = feat(e.gamma, cfg.gamma_dt(), fb, 1.f);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = post(acc[fb][tb], g, tb);
+    }
+  }
+
+  if (!cfg.quant()) {
+    emit(ydt, pairs, dy, [&](int fb, int tb) __attribute__((always_inline)) { return acc[fb][tb]; });
+    return;
+  }
+
+  // ---- FP8 per-row quantisation: publish the row absmax, meet every other feature tile of
+  // the row block, then scale by 1 / s with s = fl32(absmax / 448)
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    float m = 0.f;
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[fb][tb][r]));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    const int t = t0 + tk(tb);
+    if (hb == 0 && t < M)
+      __hip_atomic_fetch_max(ws_amax(e.ws, e.ws_rb) + t, __float_as_uint(m), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+  rendezvous_wait(e.ws, rb, a.tiles_f);
+  float inv[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int t = t0 + tk(tb);
+    inv[tb] = 0.f;
+    if (t < M) {
+      const float amax = __uint_as_float(
+          __hip_atomic_load(ws_amax(e.ws, e.ws_rb) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      const float s = __fdiv_rn(amax, 448.0f);  // IEEE division: s = fl32(a / 448)
+      inv[tb] = s > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+      if (f0 == 0 && wf == 0 && hb == 0) e.scales[t] = s;
+    }
+  }
+  emit(ydt, pairs, dy, [&](int fb, int tb) __attribute__((always_inline)) {
+    f32x16 v = acc[fb][tb];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = fminf(fmaxf(v[r] * inv[tb], -448.f), 448.f);
+    return v;
+  });
+  rendezvous_depart(e.ws, e.ws_rb, rb, a.tiles_f, t0, min(kTileRows, M - t0), slot);
+}
+
+}  // namespace fusedops

@@ -284,7 +284,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (ol.quant) {
     const int tile_f = kern == Kernel::T256 ? gemm_bf16_t256_tile_f()
                        : kern == Kernel::SKINNY ? gemm_bf16_skinny_tile_f() : gemm_f32_tile_f();
-    const void* sym = kern == Kernel::T256 ? gemm_bf16_t256_symbol()
+    const void* sym = kern == Kernel::T256 ? gemm_bf16_t256_symbol(a.ep)
                       : kern == Kernel::SKINNY ? gemm_bf16_skinny_symbol() : gemm_f32_symbol();
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||

@@ -130,23 +130,26 @@ __device__ __forceinline__ int dtype_bytes(int dtype) {
 // activations (fp32 in registers)
 // ---------------------------------------------------------------------------
 
-// erf for fp32 by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
-// 7.1.26: erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^{-x^2}, t = 1/(1 + p x),
-// x >= 0, absolute error <= 1.5e-7; odd symmetry gives x < 0. Branch-free, one exp and
-// one reciprocal. It also yields 1 + erf(x) for x < 0 without cancellation, which GELU uses.
-__device__ __forceinline__ float erfc_pos_as(float ax) {
-  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
-  const float poly =
-      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
-  return poly * __expf(-ax * ax);  // = 1 - erf(ax)
-}
-
-// GELU, erf form: 0.5 v (1 + erf(v / sqrt 2)).
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^{-x^2}, t = 1/(1 + p x), x >= 0,
+// absolute error <= 1.5e-7; odd symmetry covers x < 0. Used branch-free below, and in a
+// form that gives 1 + erf(x) for x < 0 without cancellation.
+// GELU, erf form: 0.5 v (1 + erf(v / sqrt 2)) = v Phi(v). With a = |v| / sqrt 2 the same
+// formula gives h = 0.5 erfc(a) = t Q(t) 2^{-v^2 log2(e) / 2}, t = 1 / (1 + (p / sqrt 2)|v|),
+// Q holding the five coefficients halved; then Phi(v) = 1 - h for v >= 0 and h otherwise.
+// The constant factors are folded at compile time, leaving 13 VALU ops, one v_rcp_f32 and
+// one v_exp_f32 per element.
 __device__ __forceinline__ float gelu_erf_f32(float v) {
-  const float u = v * 0.70710678118654752f;
-  const float c = erfc_pos_as(fabsf(u));            // 1 - erf(|u|)
-  const float one_plus_erf = u >= 0.f ? 2.0f - c : c;
-  return 0.5f * v * one_plus_erf;
+  constexpr double kRsqrt2 = 0.70710678118654752, kLog2e = 1.4426950408889634;
+  constexpr float P = (float)(0.3275911 * kRsqrt2);
+  constexpr float A1 = (float)(0.5 * 0.254829592), A2 = (float)(0.5 * -0.284496736),
+                  A3 = (float)(0.5 * 1.421413741), A4 = (float)(0.5 * -1.453152027),
+                  A5 = (float)(0.5 * 1.061405429);
+  constexpr float E = (float)(-0.5 * kLog2e);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(fabsf(v), P, 1.0f));
+  const float poly = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, A5, A4), A3), A2), A1);
+  const float h = poly * __builtin_amdgcn_exp2f((v * E) * v);
+  return v * (v >= 0.f ? 1.0f - h : h);
 }
 
 // GELU, tanh form. 0.5 v (1 + tanh u) equals v / (1 + e^{-2u}), which needs one exp

@@ -17,7 +17,7 @@
 // blocks (A = W rows, B = X rows, D[f][t]); the epilogue then stages the tile in LDS.
 #include <type_traits>
 
-#include "epilogue.h"
+#include "acc_epilogue.h"
 #include "kernels.h"
 
 namespace fusedops {
@@ -58,6 +58,7 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_t, int tiles_f, i
   ft = in / gt;
 }
 
+template <uint32_t F>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];  // [stage][W, X]
   __shared__ int slot[2];
@@ -211,17 +212,45 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
 #pragma clang loop unroll(disable)
   for (int s = 0; s < steps; ++s) kstep(s);
 
-  // Epilogue: the 256 x 256 fp32 tile is staged through LDS in two 128-token passes
-  // (128 KB each); pass p takes the accumulators of the waves with wt == p.
-  run_staged_epilogue<BF, 1, 128, 2>(
-      a, reinterpret_cast<float*>(smem), t0, f0, min(BT, a.M - t0), tt, slot,
-      [&](int p, float* tile) __attribute__((always_inline)) {
-        if (wt != p) return;
+  if constexpr ((F & epi::kStatic) != 0) {
+    // Epilogue on the accumulators in place; the mainloop's LDS buffers (128 KB) stage
+    // the finished values for coalesced stores.
+    acc_epilogue<F>(a, acc, smem, t0, f0, tt, slot);
+  } else {
+    // Any other op list: the fp32 tile is staged through LDS in two 128-token passes
+    // (128 KB each; pass p takes the accumulators of the waves with wt == p) and the
+    // row-layout chain reads every choice at run time.
+    run_staged_epilogue<BF, 1, 128, 2>(
+        a, reinterpret_cast<float*>(smem), t0, f0, min(BT, a.M - t0), tt, slot,
+        [&](int p, float* tile) __attribute__((always_inline)) {
+          if (wt != p) return;
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
+          for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb) stage_block<BF>(tile, acc[fb][tb], wf * 128 + fb * 32, tb * 32);
-      });
+            for (int tb = 0; tb < 4; ++tb) stage_block<BF>(tile, acc[fb][tb], wf * 128 + fb * 32, tb * 32);
+        });
+  }
+}
+
+// Epilogue configurations with an instance of their own (the op sets of the fused QKV
+// projection, MLP-up, out-projection, gate/up and FP8 gate/up layers); any other op list
+// runs the generic instance, which reads its choices at run time.
+constexpr uint32_t kCfgBiasGeluErf = epi::config(epi::kBias, ACT_GELU_ERF, FUSEDOPS_BF16);
+constexpr uint32_t kCfgBiasSplit = epi::config(epi::kBias | epi::kSplit, ACT_NONE, FUSEDOPS_BF16);
+constexpr uint32_t kCfgResidualRms = epi::config(epi::kZ | epi::kAux | epi::kPart | epi::kGamma, ACT_NONE,
+                                                 FUSEDOPS_BF16);
+constexpr uint32_t kCfgSwiglu = epi::config(0, ACT_SWIGLU, FUSEDOPS_BF16);
+constexpr uint32_t kCfgSwigluFp8 = epi::config(epi::kQuant, ACT_SWIGLU, FUSEDOPS_F8E4M3);
+
+const void* t256_kernel_for(const EpiParams& e) {
+  switch (epi::config_of(e)) {
+    case kCfgBiasGeluErf: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgBiasGeluErf>);
+    case kCfgBiasSplit: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgBiasSplit>);
+    case kCfgResidualRms: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgResidualRms>);
+    case kCfgSwiglu: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgSwiglu>);
+    case kCfgSwigluFp8: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgSwigluFp8>);
+    default: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<0>);
+  }
 }
 
 }  // namespace
@@ -231,13 +260,12 @@ hipError_t launch_gemm_bf16_t256(GemmArgs a, hipStream_t stream) {
   a.tiles_f = (a.N + BF - 1) / BF;
   const int grid = a.tiles_t * a.tiles_f;
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_bf16_t256_kernel), dim3(grid), dim3(kThreads),
-                         args, 0, stream);
+  return hipLaunchKernel(t256_kernel_for(a.ep), dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
 int gemm_bf16_t256_tile_t() { return BT; }
 int gemm_bf16_t256_tile_f() { return BF; }
 
-const void* gemm_bf16_t256_symbol() { return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel); }
+const void* gemm_bf16_t256_symbol(const EpiParams& e) { return t256_kernel_for(e); }
 
 }  // namespace fusedops

@@ -7,12 +7,14 @@
 namespace fusedops {
 
 struct GemmArgs;
+struct EpiParams;
 
-// bf16 GEMM + epilogue, 256 x 256 tiles (tokens x features), 4 waves.
+// bf16 GEMM + epilogue, 256 x 256 tiles (tokens x features), 4 waves. The kernel instance
+// depends on the epilogue configuration; the symbol is the one a call with `e` launches.
 hipError_t launch_gemm_bf16_t256(GemmArgs a, hipStream_t stream);
 int gemm_bf16_t256_tile_t();
 int gemm_bf16_t256_tile_f();
-const void* gemm_bf16_t256_symbol();
+const void* gemm_bf16_t256_symbol(const EpiParams& e);
 
 // bf16 GEMM + epilogue for few tokens (decode): 32-token x 64-feature tiles, K split
 // over the 4 waves.
