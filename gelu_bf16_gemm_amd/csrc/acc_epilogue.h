@@ -9,7 +9,8 @@
 // so each lane owns runs ("groups") of four consecutive features of four tokens: 16 groups
 // (fb, q = r / 4) per token. This is the layout the chain runs in ([Epilogue] §模式A,
 // §模式B, §仿射量化与尾声的五步; op order as in the row-layout epilogue):
-//   * per-feature vectors (bias, column scale) are 16 four-wide loads per lane, once;
+//   * per-feature vectors (bias, column scale) and the row scales are read from a small
+//     LDS copy the kernel makes before its mainloop, so their load latency is hidden;
 //   * SwiGLU pairs (2j, 2j+1) lie in one group, so gate and up meet in the same lane;
 //   * a token's sum of squares over the wave's 128 features (one RMSNorm partial chunk)
 //     is an in-lane sum over 64 registers plus one exchange with lane l ^ 32; the FP8
@@ -137,9 +138,33 @@ __device__ __forceinline__ f32x4 vec4(const void* p, int dt, int f, int N, float
   return load4(p, dt, f);
 }
 
+// The tile's per-feature and per-token vectors, copied to LDS (as fp32) before the
+// mainloop: [0] bias (0 past N), [1] column scale (1 past N), [2] row scale (0 past M).
+// Thread tid loads element tid of each vector the configuration uses; the caller stores the
+// values with `store` after issuing its own first loads, so the latency overlaps.
+struct VecPrefetch {
+  float v[3];
+  template <uint32_t F>
+  __device__ __forceinline__ void load(const EpiParams& e, int t0, int f0, int M, int N) {
+    const epi::Cfg<F> cfg{e};
+    const int tid = threadIdx.x;
+    const int f = f0 + tid, t = t0 + tid;
+    v[0] = cfg.bias() && f < N ? load1(e.bias, cfg.bias_dt(), f) : 0.f;
+    v[1] = cfg.gamma() && f < N ? load1(e.gamma, cfg.gamma_dt(), f) : 1.f;
+    v[2] = cfg.rscale() && t < M ? e.rscale[t] : 0.f;
+  }
+  __device__ __forceinline__ void store(float* svec) const {
+    const int tid = threadIdx.x;
+    svec[tid] = v[0];
+    svec[256 + tid] = v[1];
+    svec[512 + tid] = v[2];
+  }
+};
+
 // Where a staged tile's rows go in global memory.
 struct Dest {
   uint8_t* base[3];  // destination(s); more than one for a split store
+  __device__ uint8_t* at(int seg) const { return seg == 0 ? base[0] : (seg == 1 ? base[1] : base[2]); }
   int64_t ld;        // elements per row
   int64_t split_w;   // columns per destination (0: a single destination)
   int es;            // bytes per element
@@ -152,27 +177,27 @@ struct Dest {
 // and one destination, otherwise 4-byte stores of its valid words.
 __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int row0, int M, const Dest& d) {
   const int cshift = __builtin_ctz(C);
+  const int per = 16 / d.es;  // elements per chunk
+  const int sw = (int)d.split_w;
+#pragma unroll 8
   for (int id = threadIdx.x; id < R * C; id += kEpiThreads) {
     const int r = id >> cshift, c = id & (C - 1);
     const int t = row0 + r;
-    if (t >= M) continue;
-    const int col = d.col0 + c * 16 / d.es;
-    if (col >= d.cols) continue;
+    const int col = d.col0 + c * per;
+    if (t >= M || col >= d.cols) continue;
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + st_off(r, c * 16, C));
-    const int per = 16 / d.es;  // elements per chunk
-    const int seg = d.split_w ? (int)(col / d.split_w) : 0;
-    const int64_t cseg = col - (int64_t)seg * d.split_w;
-    const bool whole = col + per <= d.cols && (!d.split_w || cseg + per <= d.split_w);
+    const int seg = sw ? col / sw : 0;
+    const int cseg = col - seg * sw;
+    const bool whole = col + per <= d.cols && (!sw || cseg + per <= sw);
     if (whole) {
-      *reinterpret_cast<u32x4*>(d.base[seg] + ((int64_t)t * d.ld + cseg) * d.es) = v;
+      *reinterpret_cast<u32x4*>(d.at(seg) + ((int64_t)t * d.ld + cseg) * d.es) = v;
     } else {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int cw = col + w * 4 / d.es;  // first column of word w
         if (cw >= d.cols) break;
-        const int sw = d.split_w ? (int)(cw / d.split_w) : 0;
-        const int64_t cc = cw - (int64_t)sw * d.split_w;
-        *reinterpret_cast<uint32_t*>(d.base[sw] + ((int64_t)t * d.ld + cc) * d.es) = v[w];
+        const int sg = sw ? cw / sw : 0;
+        *reinterpret_cast<uint32_t*>(d.at(sg) + ((int64_t)t * d.ld + (cw - sg * sw)) * d.es) = v[w];
       }
     }
   }
@@ -181,11 +206,11 @@ __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int r
 }  // namespace accepi
 
 // Run the whole epilogue of one 256 x 256 tile whose accumulators are in `acc` (the
-// layout above). `lds` is at least 128 KB of LDS that the mainloop no longer uses; every
-// thread of the workgroup must call this.
+// layout above). `lds` is at least 128 KB of LDS that the mainloop no longer uses and
+// `svec` the tile's vectors (VecPrefetch); every thread of the workgroup must call this.
 template <uint32_t F>
-__device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, int t0, int f0,
-                                             int rb, int* slot) {
+__device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, const float* svec,
+                                             int t0, int f0, int rb, int* slot) {
   using namespace accepi;
   const EpiParams& e = a.ep;
   const epi::Cfg<F> cfg{e};
@@ -234,20 +259,17 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     }
   };
 
-  // per-feature vectors of feature block fb (16 values per lane)
-  auto feat = [&](const void* ptr, int dt, int fb, float fill) __attribute__((always_inline)) {
+  // per-feature vector k (0 bias, 1 column scale) of feature block fb (16 values per lane)
+  auto feat = [&](int k, int fb) __attribute__((always_inline)) {
     f32x16 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f32x4 x = vec4(ptr, dt, f0 + fl(fb, q), N, fill);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(svec + k * 256 + fl(fb, q));
       o[4 * q] = x[0]; o[4 * q + 1] = x[1]; o[4 * q + 2] = x[2]; o[4 * q + 3] = x[3];
     }
     return o;
   };
-  auto rs_of = [&](int tb) __attribute__((always_inline)) {
-    const int t = t0 + tk(tb);
-    return t < M ? e.rscale[t] : 0.f;
-  };
+  auto rs_of = [&](int tb) __attribute__((always_inline)) { return svec[512 + tk(tb)]; };
   // column scale, row scale, activation on one block (SwiGLU leaves the two outputs of
   // group q in registers 4q and 4q + 1, zeros in 4q + 2 and 4q + 3)
   auto post = [&](f32x16 v, const f32x16& g, int tb) __attribute__((always_inline)) {
@@ -294,8 +316,8 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     int fb_loaded = -1;
     emit(ydt, pairs, dy, [&](int fb, int tb) __attribute__((always_inline)) {
       if (fb != fb_loaded) {
-        if (cfg.bias()) b = feat(e.bias, cfg.bias_dt(), fb, 0.f);
-        if (cfg.gamma()) g = feat(e.gamma, cfg.gamma_dt(), fb, 1.f);
+        if (cfg.bias()) b = feat(0, fb);
+        if (cfg.gamma()) g = feat(1, fb);
         fb_loaded = fb;
       }
       f32x16 v = acc[fb][tb];
@@ -309,32 +331,47 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
   if (cfg.bias()) {
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
-      const f32x16 b = feat(e.bias, cfg.bias_dt(), fb, 0.f);
+      const f32x16 b = feat(0, fb);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[fb][tb] += b;
     }
   }
   if (cfg.z()) {
-    // coalesced copy of the residual rows into the staged-tile layout, then per-group reads;
-    // rows past M and columns past N read as zero
+    // The residual rows are copied into the staged-tile layout by LDS DMA (each wave
+    // instruction fills 1 KB: lane i lands at position 16 i, so it fetches the chunk whose
+    // swizzled position that is), all instructions in flight at once; then per-group reads.
+    // Rows past M and columns past N read as zero (out-of-range buffer offsets).
     const int zdt = cfg.z_dt();
     const int es = dt_bytes(zdt);
     const int C = kTileCols * es / 16;
     const int passes = kTileRows * kTileCols * es > kStageBytes ? 2 : 1;
     const int R = kTileRows / passes;
     const int cshift = __builtin_ctz(C);
+    const int m = (C < 32 ? C : 32) - 1;
+    const int lane_u = threadIdx.x & 63;
 #pragma clang loop unroll(disable)
     for (int p = 0; p < passes; ++p) {
+      const int rows = min(R, M - t0 - p * R);  // valid rows of this pass (>= 1 for p = 0)
       __syncthreads();
-      for (int id = threadIdx.x; id < R * C; id += kEpiThreads) {
-        const int r = id >> cshift, c = id & (C - 1);
-        const int t = t0 + p * R + r;
-        const int col = f0 + c * 16 / es;
-        u32x4 v = u32x4{0, 0, 0, 0};
-        if (t < M && col < N)
-          v = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(e.z) + ((int64_t)t * e.ldz + col) * es);
-        *reinterpret_cast<u32x4*>(lds + st_off(r, c * 16, C)) = v;
+      if (rows > 0) {
+        const uint8_t* zb = static_cast<const uint8_t*>(e.z) + ((int64_t)(t0 + p * R) * e.ldz + f0) * es;
+        const __amdgpu_buffer_rsrc_t rz =
+            make_rsrc(zb, (uint32_t)(((int64_t)(rows - 1) * e.ldz + min(kTileCols, N - f0)) * es));
+#pragma unroll 8
+        for (int j = 0; j < R * C / kEpiThreads; ++j) {
+          const int id = j * kEpiThreads + wave * 64 + lane_u;
+          const int r = id >> cshift, pos = id & (C - 1);
+          const int c = pos ^ (r & m);
+          const uint32_t oob = (uint32_t)(f0 + c * 16 / es >= N) << 31;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(lds + (j * kEpiThreads + wave * 64) * 16), 16,
+                                                   ((uint32_t)(r * e.ldz * es + c * 16)) | oob, 0, 0, 0);
+        }
+      } else {
+        // no valid rows: zero this pass's tile
+        for (int id = threadIdx.x; id < R * C; id += kEpiThreads)
+          *reinterpret_cast<u32x4*>(lds + id * 16) = u32x4{0, 0, 0, 0};
       }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
       __syncthreads();
       if (passes == 1 || wt == p) {
 #pragma unroll
@@ -377,7 +414,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
       f32x16 g = {};
-      if (cfg.gamma()) g = feat(e.gamma, cfg.gamma_dt(), fb, 1.f);
+      if (cfg.gamma()) g = feat(1, fb);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = post(acc[fb][tb], g, tb);
     }

@@ -246,9 +246,13 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   }
   const int tile_rows = kern == Kernel::T256 ? 256 : (kern == Kernel::SKINNY ? 64 : 128);
   const int tile_tok = kern == Kernel::T256 ? 256 : (kern == Kernel::SKINNY ? 32 : 64);
-  // 32-bit buffer offsets cover one tile's rows
+  // 32-bit buffer offsets cover one tile's rows (operands, and the residual rows the
+  // 256 x 256 kernel copies into LDS)
   if (((int64_t)(tile_rows - 1) * ldw + K) * es_in >= (int64_t(1) << 31) ||
       ((int64_t)(tile_tok - 1) * ldx + K) * es_in >= (int64_t(1) << 31))
+    return FUSEDOPS_ERR_UNSUPPORTED;
+  if (op_res && kern == Kernel::T256 &&
+      ((int64_t)(tile_tok - 1) * op_res->ld + 256) * dtype_size(op_res->dtype) >= (int64_t(1) << 31))
     return FUSEDOPS_ERR_UNSUPPORTED;
 
   GemmArgs a;

@@ -74,6 +74,13 @@ __device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// One element of a bf16 / fp16 / fp32 vector as fp32.
+__device__ __forceinline__ float load1(const void* base, int dtype, int64_t idx) {
+  if (dtype == FUSEDOPS_F32) return static_cast<const float*>(base)[idx];
+  const uint32_t b = static_cast<const uint16_t*>(base)[idx];
+  return dtype == FUSEDOPS_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+
 // Load 4 consecutive elements of a 1-D / row vector with a runtime dtype, as fp32.
 // `idx` must be a multiple of 4 (8-byte or 16-byte aligned access).
 __device__ __forceinline__ f32x4 load4(const void* base, int dtype, int64_t idx) {

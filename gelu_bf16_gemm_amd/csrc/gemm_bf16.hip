@@ -61,6 +61,7 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_t, int tiles_f, i
 template <uint32_t F>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];  // [stage][W, X]
+  __shared__ __attribute__((aligned(16))) float svec[3 * 256];               // epilogue vectors
   __shared__ int slot[2];
 
   const int tid = threadIdx.x;
@@ -80,6 +81,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   }
   const int f0 = ft * BF, t0 = tt * BT;
   const int K = a.K;
+
+  // the epilogue's per-feature / per-token vectors, fetched now and kept in LDS
+  accepi::VecPrefetch vp;
+  if constexpr ((F & epi::kStatic) != 0) vp.load<F>(a.ep, t0, f0, a.M, a.N);
 
   // Buffer resources over this tile's rows: rows past M / N read as zero.
   const int w_rows = min(BF, a.N - f0), x_rows = min(BT, a.M - t0);
@@ -207,6 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   for (int q = 0; q < 4; ++q) store_q(0, q);
 #pragma unroll
   for (int q = 0; q < 4; ++q) load_q(BK, q);
+  if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
   __syncthreads();
 
 #pragma clang loop unroll(disable)
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   if constexpr ((F & epi::kStatic) != 0) {
     // Epilogue on the accumulators in place; the mainloop's LDS buffers (128 KB) stage
     // the finished values for coalesced stores.
-    acc_epilogue<F>(a, acc, smem, t0, f0, tt, slot);
+    acc_epilogue<F>(a, acc, smem, svec, t0, f0, tt, slot);
   } else {
     // Any other op list: the fp32 tile is staged through LDS in two 128-token passes
     // (128 KB each; pass p takes the accumulators of the waves with wt == p) and the
