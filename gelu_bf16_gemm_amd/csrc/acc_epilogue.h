@@ -210,7 +210,7 @@ __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int r
 // `svec` the tile's vectors (VecPrefetch); every thread of the workgroup must call this.
 template <uint32_t F>
 __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, const float* svec,
-                                             int t0, int f0, int rb, int* slot) {
+                                             int t0, int f0, int rb, int ft, int* slot) {
   using namespace accepi;
   const EpiParams& e = a.ep;
   const epi::Cfg<F> cfg{e};
@@ -425,8 +425,12 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     return;
   }
 
-  // ---- FP8 per-row quantisation: publish the row absmax, meet every other feature tile of
-  // the row block, then scale by 1 / s with s = fl32(absmax / 448)
+  // ---- FP8 per-row quantisation: publish this tile's row absmax in its own workspace slots,
+  // meet every other column tile of the row block, reduce the slots of the tile's rows, then
+  // scale by 1 / s with s = fl32(absmax / 448)
+  float* s_half = reinterpret_cast<float*>(lds);  // [2][256]: per feature half (wf)
+  float* s_amax = s_half + 2 * kTileRows;         // [256]: row absmax over all column tiles
+  __syncthreads();
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     float m = 0.f;
@@ -435,24 +439,25 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[fb][tb][r]));
     m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    const int t = t0 + tk(tb);
-    if (hb == 0 && t < M)
-      __hip_atomic_fetch_max(ws_amax(e.ws, e.ws_rb) + t, __float_as_uint(m), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+    if (hb == 0) s_half[wf * kTileRows + tk(tb)] = m;
   }
-  rendezvous_wait(e.ws, rb, a.tiles_f);
+  __syncthreads();
+  {
+    const int i = threadIdx.x, t = t0 + i;
+    if (t < M) publish_row_amax(e, ft, t, fmaxf(s_half[i], s_half[kTileRows + i]));
+  }
+  rendezvous_wait(e, rb, ft, a.tiles_f);
+  reduce_row_amax<kTileRows>(e, a.tiles_f, t0, min(kTileRows, M - t0), s_amax);
+  __syncthreads();
+  {
+    const int i = threadIdx.x, t = t0 + i;
+    if (f0 == 0 && t < M) e.scales[t] = __fdiv_rn(s_amax[i], 448.0f);
+  }
   float inv[4];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const int t = t0 + tk(tb);
-    inv[tb] = 0.f;
-    if (t < M) {
-      const float amax = __uint_as_float(
-          __hip_atomic_load(ws_amax(e.ws, e.ws_rb) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      const float s = __fdiv_rn(amax, 448.0f);  // IEEE division: s = fl32(a / 448)
-      inv[tb] = s > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
-      if (f0 == 0 && wf == 0 && hb == 0) e.scales[t] = s;
-    }
+    const float s = __fdiv_rn(s_amax[tk(tb)], 448.0f);  // IEEE division: s = fl32(a / 448)
+    inv[tb] = s > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
   }
   emit(ydt, pairs, dy, [&](int fb, int tb) __attribute__((always_inline)) {
     f32x16 v = acc[fb][tb];
@@ -460,7 +465,6 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     for (int r = 0; r < 16; ++r) v[r] = fminf(fmaxf(v[r] * inv[tb], -448.f), 448.f);
     return v;
   });
-  rendezvous_depart(e.ws, e.ws_rb, rb, a.tiles_f, t0, min(kTileRows, M - t0), slot);
 }
 
 }  // namespace fusedops

@@ -79,10 +79,15 @@ int32_t parse_ops(const fusedops_op* ops, int32_t n_ops, OpList& out) {
   return FUSEDOPS_OK;
 }
 
-// Row blocks reserved in the FP8 workspace: enough for the finest token tile (32).
+// FP8 workspace: a control record per row block of the finest token tile (32 tokens) with
+// one 128-byte line per counter (groups of 16 column tiles of the finest feature tile, 64
+// features), and per token one absmax slot per column tile, rounded up to a multiple of 4
+// slots so each token's slots start 16-byte aligned.
 int64_t ws_row_blocks(int64_t M) { return cdiv(M, 32); }
-size_t ws_bytes_for(int64_t M) {
-  const int64_t words = 2 + 2 * ws_row_blocks(M) + M;
+int64_t ws_slots_per_token(int64_t N) { return cdiv(cdiv(N, 64), 4) * 4; }
+int64_t ws_groups(int64_t N) { return cdiv(cdiv(N, 64), 16); }
+size_t ws_bytes_for(int64_t M, int64_t N) {
+  const int64_t words = 32 + 32 * (2 + ws_groups(N)) * ws_row_blocks(M) + M * ws_slots_per_token(N);
   return (size_t)(cdiv(words * 4, 256) * 256);
 }
 
@@ -121,7 +126,7 @@ size_t fusedops_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, const fu
   (void)K;
   OpList ol;
   if (M < 1 || parse_ops(ops, n_ops, ol) != FUSEDOPS_OK) return 0;
-  return ol.quant ? ws_bytes_for(M) : 0;
+  return ol.quant ? ws_bytes_for(M, N) : 0;
 }
 
 int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int64_t ldw,
@@ -227,7 +232,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
 
   // ---- workspace
   if (ol.quant) {
-    if (!workspace || workspace_bytes < ws_bytes_for(M) || !aligned(workspace, 4)) return FUSEDOPS_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < ws_bytes_for(M, N) || !aligned(workspace, 16)) return FUSEDOPS_ERR_WORKSPACE;
     const Span sw{reinterpret_cast<uintptr_t>(workspace),
                   reinterpret_cast<uintptr_t>(workspace) + workspace_bytes, true};
     for (int o = 0; o < n_out_spans; ++o)
@@ -272,6 +277,8 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
     e.scales = static_cast<float*>(op_q->out);
     e.ws = static_cast<uint32_t*>(workspace);
     e.ws_rb = (int)ws_row_blocks(M);
+    e.ws_s = (int)ws_slots_per_token(N);
+    e.ws_g = (int)ws_groups(N);
   }
   e.y = Y; e.ldy = ldy; e.y_dtype = out_dtype;
   if (op_split) {
@@ -296,6 +303,9 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sym, 256, 0) != hipSuccess)
       return launch_status(hipErrorInvalidValue, "occupancy query");
     if (cdiv(N, tile_f) > (int64_t)cus * per_cu) return FUSEDOPS_ERR_UNSUPPORTED;
+    // Tiles are handed out in row-block-major ticket order only when the grid does not fit
+    // on the device at once; otherwise every tile is resident and any order is safe.
+    a.ep.tickets = cdiv(M, tile_tok) * cdiv(N, tile_f) > (int64_t)cus * per_cu ? 1 : 0;
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);

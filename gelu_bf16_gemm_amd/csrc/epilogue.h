@@ -37,6 +37,9 @@ struct EpiParams {
   float* scales;
   uint32_t* ws;           // rendezvous workspace (quant only)
   int ws_rb;              // row-block counters reserved in the workspace
+  int ws_s;               // absmax slots per token in the workspace
+  int ws_g;               // column-tile groups per row-block control record
+  int tickets;            // hand out tiles by ticket (the grid exceeds what is resident at once)
   void* y;                int64_t ldy;     int y_dtype;
   int n_split;            int64_t split_w; int64_t ldv;
   void* yv0;              void* yv1;       void* yv2;
@@ -57,16 +60,68 @@ constexpr int kEpiThreads = 256;
 // ---------------------------------------------------------------------------
 // Workspace layout (uint32 words):
 //   [0]                error word: set to 1 if a wait ever hit its spin bound (never cleared here)
-//   [1]                tile ticket counter
-//   [2, 2+R)           arrivals per row block
-//   [2+R, 2+2R)        departures per row block
-//   [2+2R, 2+2R+M)     per-row absmax as float bits (non-negative floats order like uint32)
-// Every word except [0] is back at zero when the kernel ends.
+//   [1]                tile ticket counter (back at zero after every call)
+//   [32 + CR rb ...]   control record of row block rb, CR = 32 (2 + G) words, one counter per
+//                      128-byte line: line 0 counts arriving groups, line 1 is the release
+//                      flag (a generation count: it goes up by one per call), line 2 + g counts
+//                      the arrivals of column-tile group g (kGroupTiles tiles each; G = ws_g)
+//   [B, ...)           row absmax slots, float bits, from B = 32 + CR R, S words per token
+//                      (S = ws_s, a multiple of 4): word B + t*S + ft holds the absmax of
+//                      token t over the features of column tile ft
+// Each tile writes its own slots; no two tiles touch the same word. The arrival counters
+// are reset by the tile that completes them, and the flag is only ever compared with the
+// value a tile saw before arriving, so nothing needs clearing after a call: the workspace
+// must be zero-filled once after allocation and then handed to every call unchanged.
+//
+// Memory ordering. Each XCD has its own L2; agent-scope release / acquire fences are
+// L2-wide write-back / invalidate operations that would disturb every other tile on the XCD.
+// The rendezvous avoids them: every word other tiles read is written and read with the
+// agent-scope coherence policy (sc1, the policy of agent-scope atomic loads and stores),
+// which makes the access at the device's coherence point. A tile's slot stores complete
+// (s_waitcnt) before its thread 0 arrives; the flag is raised only after every arrival
+// has been counted, and slots are read only after the raised flag was seen, so the reads
+// return the published values.
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kGroupTiles = 16;
+constexpr int kPolicyCoherent = 16;  // sc1: agent-scope coherence policy of a buffer access
 
-__device__ __forceinline__ uint32_t* ws_arrive(uint32_t* ws) { return ws + 2; }
-__device__ __forceinline__ uint32_t* ws_depart(uint32_t* ws, int R) { return ws + 2 + R; }
-__device__ __forceinline__ uint32_t* ws_amax(uint32_t* ws, int R) { return ws + 2 + 2 * R; }
+__device__ __forceinline__ uint32_t* ws_ctl(const EpiParams& e, int rb) {
+  return e.ws + 32 + 32 * (2 + e.ws_g) * rb;
+}
+__device__ __forceinline__ uint32_t* ws_slots(const EpiParams& e) {
+  return e.ws + 32 + 32 * (2 + e.ws_g) * e.ws_rb;
+}
+
+// Publish the absmax m of token t over column tile ft.
+__device__ __forceinline__ void publish_row_amax(const EpiParams& e, int ft, int t, float m) {
+  __hip_atomic_store(ws_slots(e) + (int64_t)t * e.ws_s + ft, __float_as_uint(m), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// After the row block's rendezvous: out[i] = absmax of token t0 + i over all `tiles_f`
+// column tiles, for i < nrows. ROWS rows (a power of two dividing the 256 threads) share the
+// workgroup: 256 / ROWS threads per row, each taking 16-byte runs of the row's slots with
+// all of its loads in flight. Slots past tiles_f in a row are never written, so zero.
+template <int ROWS>
+__device__ __forceinline__ void reduce_row_amax(const EpiParams& e, int tiles_f, int t0, int nrows, float* out) {
+  constexpr int TPR = 256 / ROWS;
+  static_assert(TPR >= 1 && TPR <= 64 && 256 % ROWS == 0, "threads per row");
+  const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(ws_slots(e) + (int64_t)t0 * e.ws_s, (uint32_t)(nrows * e.ws_s * 4));
+  uint32_t m = 0;  // non-negative floats order like their bit patterns
+  if (row < nrows) {
+#pragma unroll 8
+    for (int j = part * 4; j < tiles_f; j += TPR * 4) {
+      const u32x4 v = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((row * e.ws_s + j) * 4), 0, kPolicyCoherent));
+      m = max(m, max(max(v[0], v[1]), max(v[2], v[3])));
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+  if (row < nrows && part == 0) out[row] = __uint_as_float(m);
+}
 
 // Take the next tile ticket (thread 0 draws, the block shares it through LDS). The block
 // that draws the last ticket resets the counter: every other ticket was already drawn.
@@ -83,46 +138,35 @@ __device__ __forceinline__ int draw_ticket(uint32_t* ws, int total, int* lds_slo
   return t;
 }
 
-// Arrive at row block `rb` and wait until all `need` tiles of it have arrived. Every
-// tile publishes its absmax contribution before arriving, so once the count is complete
-// the per-row maxima are final. The wait is bounded; on timeout the error word is set.
-__device__ __forceinline__ void rendezvous_wait(uint32_t* ws, int rb, int need) {
-  __threadfence();
+// Arrive at row block `rb` as column tile ft and wait until all `need` column tiles of the
+// block have arrived (every tile publishes its absmax slots first). Arrivals are counted in
+// groups of kGroupTiles on separate lines, so no counter sees more than a few dozen
+// atomics; the tile that completes the last group raises the block's flag. The wait is
+// bounded; on timeout the error word is set.
+__device__ __forceinline__ void rendezvous_wait(const EpiParams& e, int rb, int ft, int need) {
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's slot stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t* arrive = ws_arrive(ws) + rb;
-    __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t it = 0;
-    while (__hip_atomic_load(arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)need) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++it > kSpinLimit) {
-        __hip_atomic_store(ws, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
+    uint32_t* rec = ws_ctl(e, rb);
+    uint32_t* flag = rec + 32;
+    const uint32_t gen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int g = ft / kGroupTiles, groups = (need + kGroupTiles - 1) / kGroupTiles;
+    const int in_group = min(kGroupTiles, need - g * kGroupTiles);
+    uint32_t* gc = rec + 64 + 32 * g;
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)in_group - 1) {
+      __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(rec, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)groups - 1) {
+        __hip_atomic_store(rec, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(flag, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  }
-  __syncthreads();
-  __threadfence();
-}
-
-// Leave row block `rb`; the last tile to leave clears the block's counters and the absmax
-// of its rows [t0, t0 + ntok) so the workspace is zero again for the next call.
-__device__ __forceinline__ void rendezvous_depart(uint32_t* ws, int R, int rb, int need, int t0,
-                                                  int ntok, int* lds_slot) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t old = __hip_atomic_fetch_add(ws_depart(ws, R) + rb, 1u, __ATOMIC_ACQ_REL,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-    *lds_slot = (old == (uint32_t)need - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (*lds_slot) {
-    uint32_t* amax = ws_amax(ws, R);
-    for (int i = threadIdx.x; i < ntok; i += blockDim.x)
-      __hip_atomic_store(amax + t0 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) {
-      __hip_atomic_store(ws_arrive(ws) + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ws_depart(ws, R) + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t it = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++it > kSpinLimit) {
+        __hip_atomic_store(e.ws, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
     }
   }
   __syncthreads();
@@ -206,7 +250,7 @@ enum EpiMode {
 // of the block must call this (it contains wave-wide shuffles but no barriers).
 template <int COLS, int NSRC, int ROWS_ALLOC>
 __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* tile, int t0,
-                                              int nrows, int f0, int mode) {
+                                              int nrows, int f0, int ft, const float* amax_rows, int mode) {
   constexpr int TPR = COLS / 8;            // threads per row
   constexpr int RPI = kEpiThreads / TPR;   // rows per iteration
   static_assert(TPR <= 64 && 64 % TPR == 0, "a row's threads must sit in one wave");
@@ -310,13 +354,10 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
       if (!f_ok) m = 0.f;
 #pragma unroll
       for (int o = 1; o < TPR; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-      if (g == 0 && t_ok)
-        __hip_atomic_fetch_max(ws_amax(e.ws, e.ws_rb) + t, __float_as_uint(m), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+      if (g == 0 && t_ok) publish_row_amax(e, ft, t, m);
     } else {
       if (!t_ok) continue;
-      const float amax = __uint_as_float(
-          __hip_atomic_load(ws_amax(e.ws, e.ws_rb) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      const float amax = amax_rows[r];
       const float s = __fdiv_rn(amax, 448.0f);  // IEEE division: s = fl32(a / 448)
       const float inv = s > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
       if (f0 == 0 && g == 0) e.scales[t] = s;
@@ -344,14 +385,18 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
 // after every column tile of the token block has done so, to quantise.
 template <int COLS, int NSRC, int ROWS, int PASSES, typename StageFn>
 __device__ __forceinline__ void run_staged_epilogue(const GemmArgs& a, float* tile, int t0, int f0,
-                                                    int nrows_total, int rb, int* lds_slot,
-                                                    StageFn&& stage) {
+                                                    int nrows_total, int rb, int ft, int* lds_slot,
+                                                    float* lds_amax, StageFn&& stage) {
   const EpiParams& e = a.ep;
   const int rounds = e.quant ? 2 : 1;
   // rolled loops: one inlined copy of the chain serves every round and pass
 #pragma clang loop unroll(disable)
   for (int round = 0; round < rounds; ++round) {
-    if (round == 1) rendezvous_wait(e.ws, rb, a.tiles_f);
+    if (round == 1) {
+      rendezvous_wait(e, rb, ft, a.tiles_f);
+      // every column tile of the row block has published: reduce this tile's rows once
+      reduce_row_amax<ROWS * PASSES>(e, a.tiles_f, t0, nrows_total, lds_amax);
+    }
     const int mode = e.quant ? (round == 0 ? EPI_AMAX : EPI_QUANT) : EPI_STORE;
 #pragma clang loop unroll(disable)
     for (int p = 0; p < PASSES; ++p) {
@@ -360,10 +405,9 @@ __device__ __forceinline__ void run_staged_epilogue(const GemmArgs& a, float* ti
       __syncthreads();
       stage(p, tile);
       __syncthreads();
-      epilogue_pass<COLS, NSRC, ROWS>(a, tile, t0 + p * ROWS, rows, f0, mode);
+      epilogue_pass<COLS, NSRC, ROWS>(a, tile, t0 + p * ROWS, rows, f0, ft, lds_amax + p * ROWS, mode);
     }
   }
-  if (e.quant) rendezvous_depart(e.ws, e.ws_rb, rb, a.tiles_f, t0, nrows_total, lds_slot);
 }
 
 }  // namespace fusedops

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   const int wf = wave >> 1, wt = wave & 1;
 
   int tt, ft;
-  if (a.ep.quant) {
+  if (a.ep.quant && a.ep.tickets) {
     // FP8 row scales need every feature tile of a token block: hand out tiles in
     // row-block-major ticket order so no block waits on a tile that is not running.
     const int ticket = draw_ticket(a.ep.ws, a.tiles_t * a.tiles_f, slot);
@@ -221,13 +221,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   if constexpr ((F & epi::kStatic) != 0) {
     // Epilogue on the accumulators in place; the mainloop's LDS buffers (128 KB) stage
     // the finished values for coalesced stores.
-    acc_epilogue<F>(a, acc, smem, svec, t0, f0, tt, slot);
+    acc_epilogue<F>(a, acc, smem, svec, t0, f0, tt, ft, slot);
   } else {
     // Any other op list: the fp32 tile is staged through LDS in two 128-token passes
     // (128 KB each; pass p takes the accumulators of the waves with wt == p) and the
     // row-layout chain reads every choice at run time.
+    __shared__ float s_amax[BT];
     run_staged_epilogue<BF, 1, 128, 2>(
-        a, reinterpret_cast<float*>(smem), t0, f0, min(BT, a.M - t0), tt, slot,
+        a, reinterpret_cast<float*>(smem), t0, f0, min(BT, a.M - t0), tt, ft, slot, s_amax,
         [&](int p, float* tile) __attribute__((always_inline)) {
           if (wt != p) return;
 #pragma unroll

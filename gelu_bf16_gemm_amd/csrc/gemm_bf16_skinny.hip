@@ -27,6 +27,7 @@ constexpr int kThreads = 256;
 __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmArgs a) {
   // two staged 32 x 64 fp32 tiles, one per K half, summed by the epilogue
   __shared__ __attribute__((aligned(16))) float lds[2 * BT * BF];
+  __shared__ float s_amax[BT];
   __shared__ int slot[2];
 
   const int tid = threadIdx.x;
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmArgs a) 
   const int h = lane >> 5;
 
   int tt, ft;
-  if (a.ep.quant) {
+  if (a.ep.quant && a.ep.tickets) {
     const int ticket = draw_ticket(a.ep.ws, a.tiles_t * a.tiles_f, slot);
     tt = ticket / a.tiles_f;
     ft = ticket - tt * a.tiles_f;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmArgs a) 
                                                       __builtin_bit_cast(bf16x8, xv[u][s]), acc, 0, 0, 0);
   }
 
-  run_staged_epilogue<BF, 2, BT, 1>(a, lds, t0, f0, min(BT, a.M - t0), tt, slot,
+  run_staged_epilogue<BF, 2, BT, 1>(a, lds, t0, f0, min(BT, a.M - t0), tt, ft, slot, s_amax,
                                     [&](int, float* tile) {
                                       stage_block<BF>(tile + kh * BT * BF, acc, fb * 32, 0);
                                     });

@@ -21,6 +21,7 @@ constexpr int kThreads = 256;
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
   // mainloop operands, then (after the loop) the staged 64 x 128 fp32 output tile
   __shared__ __attribute__((aligned(16))) float lds[BT * BF > (BF + BT) * PAD ? BT * BF : (BF + BT) * PAD];
+  __shared__ float s_amax[BT];
   __shared__ int slot[2];
   float* wl = lds;
   float* xl = lds + BF * PAD;
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
 
   int tt, ft;
-  if (a.ep.quant) {
+  if (a.ep.quant && a.ep.tickets) {
     const int ticket = draw_ticket(a.ep.ws, a.tiles_t * a.tiles_f, slot);
     tt = ticket / a.tiles_f;
     ft = ticket - tt * a.tiles_f;
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
     __syncthreads();
   }
 
-  run_staged_epilogue<BF, 1, BT, 1>(a, lds, t0, f0, min(BT, a.M - t0), tt, slot,
+  run_staged_epilogue<BF, 1, BT, 1>(a, lds, t0, f0, min(BT, a.M - t0), tt, ft, slot, s_amax,
                                     [&](int, float* tile) {
                                       stage_block<BF>(tile, acc[0][0], wave * 32, 0);
                                       stage_block<BF>(tile, acc[0][1], wave * 32, 32);

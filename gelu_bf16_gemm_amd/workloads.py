@@ -117,8 +117,12 @@ class LinearRun:
             out["scales"] = _host64(self.scales.index_select(0, idx))
         return out
 
-    def workspace_clean(self) -> bool:
-        return self.ws is None or int(self.ws.abs().sum().item()) == 0
+    def workspace_ok(self) -> bool:
+        """No row rendezvous gave up (error word 0) and the ticket counter is back at zero."""
+        if self.ws is None:
+            return True
+        w = self.ws[:2].cpu().numpy()
+        return int(w[0]) == 0 and int(w[1]) == 0
 
     # algorithmic work of one pass
     def flops(self) -> float:

@@ -141,10 +141,16 @@ typedef struct fusedops_op {
  *          in {BF16, F16, F32}, or F8E4M3 exactly when QUANT_FP8_ROW is present.
  *          Must be NULL when SPLIT_COLS is present.
  *   workspace / workspace_bytes
- *          Device scratch of at least fusedops_linear_workspace_bytes(...) bytes (0 when no op
- *          needs one; then workspace may be NULL). It must be zero-filled once after allocation;
- *          every successful call leaves it zero-filled again. Two calls that run concurrently
- *          (different streams) must not share a workspace.
+ *          Device scratch of at least fusedops_linear_workspace_bytes(...) bytes, 16-byte
+ *          aligned (0 bytes when no op needs one; then workspace may be NULL). Only
+ *          QUANT_FP8_ROW uses it: per 32-token row block, arrival counters and a release flag
+ *          for the row rendezvous, and per token one absmax slot per 64-feature column tile
+ *          (about 4 * M * N / 64 bytes in all). Zero-fill it once after allocation, then pass
+ *          it unchanged to every call: the library keeps state in it between calls (release
+ *          flags count calls; slots hold the last call's maxima). Its first 32-bit word is an
+ *          error word the kernels set to 1 if a row rendezvous ever gave up waiting (the
+ *          quantised output of that call is then unreliable); the library never clears it.
+ *          Calls that may run concurrently (different streams) must not share a workspace.
  *   stream hipStream_t.
  * Outputs are written in fp32 -> out dtype with round-to-nearest-even.
  * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE, LAUNCH (see enum).

@@ -104,3 +104,10 @@ def check_fp8(codes: np.ndarray, scales: np.ndarray, vref: np.ndarray, what: str
     q_ref = O.quantize_fp8_rows(vref, scales)
     d = np.abs(O.e4m3_ordinal(codes) - O.e4m3_ordinal(q_ref))
     assert (d <= 1).all(), f"{what}: {int((d > 1).sum())} codes more than 1 ulp away (max {d.max()})"
+
+
+def workspace_ok(ws) -> bool:
+    """The FP8 workspace after a call: no rendezvous gave up waiting (error word 0) and the
+    tile ticket counter is back at zero (the rest of the workspace is the library's state)."""
+    w = ws[:2].cpu().numpy()
+    return int(w[0]) == 0 and int(w[1]) == 0

@@ -14,7 +14,7 @@ import torch
 import oracle as O
 from gelu_bf16_gemm_amd import inputs as I
 
-from helpers import Guarded, check_f32, check_fp8, check_lowp, check_out, dev, host64, note
+from helpers import workspace_ok, Guarded, check_f32, check_fp8, check_lowp, check_out, dev, host64, note
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +117,7 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
         a_ref = np.abs(ref["y"]).max(axis=1)
         s_ref = O.fp8_row_scale(a_ref).astype(np.float64)
         np.testing.assert_allclose(s.astype(np.float64), s_ref, rtol=2e-4, atol=1e-30)
-        assert int(ws.abs().sum().item()) == 0, "workspace not left zero-filled"
+        assert workspace_ok(ws), "a row rendezvous gave up or the ticket counter was not reset"
     elif split:
         d = N // split
         for i, sg in enumerate(keep["split"]):
@@ -276,7 +276,32 @@ def test_fp8_tier1_exact_scales_and_codes():
     assert bad.size == 0, f"{len(bad)} codes differ: " + ", ".join(
         f"v={X32[m, j] / s_ref[m]!r} gpu={got[m, j]:#04x} ref={q_ref[m, j]:#04x}" for m, j in bad[:10])
     assert y.intact()
-    assert int(ws.abs().sum().item()) == 0
+    assert workspace_ok(ws)
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 4160, 64), (300, 1056, 136)])
+def test_fp8_workspace_reused_across_calls(M, N, K):
+    """One workspace, several quantised calls in a row on different inputs (the release
+    flags count calls, the slots keep the previous call's maxima): every call is exact."""
+    rng = np.random.default_rng(21)
+    ops_s = torch.empty(M, dtype=torch.float32, device="cuda")
+    ops = [B.op(B.OP_SWIGLU), B.op(B.OP_QUANT_FP8_ROW, out=ops_s)]
+    ws = torch.zeros(B.fusedops_linear_workspace_bytes(M, N, K, ops) // 4, dtype=torch.int32, device="cuda")
+    y = torch.empty((M, N // 2), dtype=torch.uint8, device="cuda")
+    y32 = torch.empty((M, N // 2), dtype=torch.float32, device="cuda")
+    for call in range(3):
+        X = I.random_stored(rng, (M, K), I.BF16, std=1.0 + call)
+        W = I.random_stored(rng, (N, K), I.BF16, std=K ** -0.5)
+        Xd, Wd = dev(X, I.BF16), dev(W, I.BF16)
+        note(f"fp8 workspace reuse call {call}")
+        assert B.fusedops_linear_epilogue(Xd, Wd, y, ops=ops, workspace=ws, out_dtype=I.F8E4M3) == B.OK
+        assert B.fusedops_linear_epilogue(Xd, Wd, y32, ops=[B.op(B.OP_SWIGLU)]) == B.OK
+        torch.cuda.synchronize()
+        assert workspace_ok(ws)
+        v = host64(y32)
+        s = host64(ops_s).astype(np.float32)
+        assert np.array_equal(s, O.fp8_row_scale(np.abs(v).max(axis=1).astype(np.float32))), f"call {call}"
+        check_fp8(host64(y), s, v, f"call {call} codes")
 
 
 def test_fp32_linear_gelu_full_size():
