@@ -297,10 +297,11 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
                        : kern == Kernel::SKINNY ? gemm_bf16_skinny_tile_f() : gemm_f32_tile_f();
     const void* sym = kern == Kernel::T256 ? gemm_bf16_t256_symbol(a.ep)
                       : kern == Kernel::SKINNY ? gemm_bf16_skinny_symbol() : gemm_f32_symbol();
+    const int threads = kern == Kernel::SKINNY ? gemm_bf16_skinny_threads() : 256;
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sym, 256, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sym, threads, 0) != hipSuccess)
       return launch_status(hipErrorInvalidValue, "occupancy query");
     if (cdiv(N, tile_f) > (int64_t)cus * per_cu) return FUSEDOPS_ERR_UNSUPPORTED;
     // Tiles are handed out in row-block-major ticket order only when the grid does not fit

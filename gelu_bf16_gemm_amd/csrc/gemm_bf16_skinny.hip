@@ -2,15 +2,19 @@
 // weight stream ([Epilogue] §边界五 and §端到端账本: with few tokens the weight read
 // dominates), so the kernel is built to keep HBM busy rather than the matrix cores.
 //
-// A workgroup owns 64 features x 32 tokens. Its 4 waves split the work as
-// (feature block fb = w & 1) x (K half kh = w >> 1): each wave streams 32 W rows over
-// every other 64-wide K block straight from HBM into MFMA operand registers (no LDS),
-// so each lane reads 64 contiguous bytes of one row per block and a pair of lanes
-// covers a full 128-byte line. Within a block, lane half h supplies K elements
-// [32 h, 32 h + 32) of the block, 8 per MFMA step, for both operands alike, which is
-// a fixed permutation of K and leaves the dot products unchanged.
-// The two K halves are staged as two fp32 tiles in LDS and summed, in a fixed order, by
-// the shared epilogue.
+// A workgroup owns 64 features x 32 tokens and has 8 waves. W streams in stages of
+// 64 rows x 256 K (32 KB): each load instruction reads 1 KB of memory as two 512-byte row
+// segments, so HBM is read in linear runs rather than in the row-strided 16-byte pieces
+// MFMA operands would need straight from memory. W loads run DR stages ahead in a register
+// ring, and each workgroup walks the stages in its own rotated order, so at any moment the
+// workgroups read different offsets of their rows rather than all the same one (measured:
+// deeper rings and longer stages were slower). One stage before it is needed a stage is
+// written into one of two LDS buffers, where a row's 16-byte chunk c sits at position
+// c ^ (row % 32) so that both the 64-lane writes and the 32-row MFMA operand reads are free
+// of bank conflicts. Wave w multiplies feature half w % 2 over the 64-wide K quarter w / 2
+// of every stage; its X operand (32 token rows, read by every workgroup) comes from L2
+// straight into registers, in a ring of its own. The four K-quarter partial tiles of each
+// feature half are staged in LDS and summed, in a fixed order, by the shared epilogue.
 #include "epilogue.h"
 #include "kernels.h"
 
@@ -20,19 +24,24 @@ namespace {
 
 constexpr int BF = 64;
 constexpr int BT = 32;
-constexpr int KB = 64;        // K block
-constexpr int UNROLL = 4;     // K blocks in flight per wave
-constexpr int kThreads = 256;
+constexpr int KS = 256;                      // K per stage
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowBytes = KS * 2;            // 512 bytes of a W row per stage
+constexpr int kBufBytes = BF * kRowBytes;    // 32 KB
+constexpr int DR = 2;                        // W stages in flight in registers
+constexpr int DX = 2;                        // X stages in flight in registers (L2 hits)
 
-__global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmArgs a) {
-  // two staged 32 x 64 fp32 tiles, one per K half, summed by the epilogue
-  __shared__ __attribute__((aligned(16))) float lds[2 * BT * BF];
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_skinny_kernel(GemmArgs a) {
+  // two stage buffers; afterwards they hold the 4 partial 32 x 64 fp32 tiles (32 KB) the
+  // epilogue sums
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBufBytes];
   __shared__ float s_amax[BT];
   __shared__ int slot[2];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int fb = wave & 1, kh = wave >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int fb = wave & 1, kq = wave >> 1;
   const int h = lane >> 5;
 
   int tt, ft;
@@ -50,38 +59,87 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmArgs a) 
   const int w_rows = min(BF, a.N - f0), x_rows = min(BT, a.M - t0);
   const uint16_t* Wt = static_cast<const uint16_t*>(a.W) + (int64_t)f0 * a.ldw;
   const uint16_t* Xt = static_cast<const uint16_t*>(a.X) + (int64_t)t0 * a.ldx;
+  // rows past N / M and chunks past K read as zero
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wt, (uint32_t)(((int64_t)(w_rows - 1) * a.ldw + K) * 2));
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xt, (uint32_t)(((int64_t)(x_rows - 1) * a.ldx + K) * 2));
 
-  const uint32_t w_row_off = (uint32_t)((fb * 32 + (lane & 31)) * a.ldw * 2);
-  const uint32_t x_row_off = (uint32_t)((lane & 31) * a.ldx * 2);
-
-  f32x16 acc = {};
-  const int nkb = (K + KB - 1) / KB;
-  for (int kb0 = kh; kb0 < nkb; kb0 += 2 * UNROLL) {
-    u32x4 wv[UNROLL][4], xv[UNROLL][4];
+  // W load i (0..3) of a stage: rows 8 wave + 2 i + h, chunk lane % 32 (8 K elements)
+  const int lc = lane & 31;
+  uint32_t w_voff[4], w_lds[4];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int kb = kb0 + 2 * u;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int k = kb * KB + h * 32 + s * 8;
-        const bool ok = kb < nkb && k < K;
-        wv[u][s] = buffer_load_16B(rW, ok ? w_row_off + (uint32_t)k * 2 : kOobOffset);
-        xv[u][s] = buffer_load_16B(rX, ok ? x_row_off + (uint32_t)k * 2 : kOobOffset);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv[u][s]),
-                                                      __builtin_bit_cast(bf16x8, xv[u][s]), acc, 0, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 8 + 2 * i + h;
+    w_voff[i] = (uint32_t)(r * a.ldw * 2 + lc * 16);
+    w_lds[i] = (uint32_t)(r * kRowBytes + ((lc ^ (r & 31)) << 4));
   }
+  // X operand of MFMA step j (0..3) of the wave's K quarter: lane half h supplies K elements
+  // [8h, 8h + 8) of the step, as the MFMA does for W
+  const uint32_t x_voff = (uint32_t)((lane & 31) * a.ldx * 2 + (kq * 64 + h * 8) * 2);
+  // W operand of step j: row wr of the stage, chunk kq * 8 + 2 j + h
+  const int wr = fb * 32 + (lane & 31);
+  uint32_t f_lds[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f_lds[j] = (uint32_t)(wr * kRowBytes + (((kq * 8 + 2 * j + h) ^ (wr & 31)) << 4));
 
-  run_staged_epilogue<BF, 2, BT, 1>(a, lds, t0, f0, min(BT, a.M - t0), tt, ft, slot, s_amax,
-                                    [&](int, float* tile) {
-                                      stage_block<BF>(tile + kh * BT * BF, acc, fb * 32, 0);
+  const int stages = (K + KS - 1) / KS;
+  u32x4 wreg[DR][4], xreg[DX][4];
+  auto load_w = [&](int s, int d) __attribute__((always_inline)) {
+    const uint32_t k0 = (uint32_t)(s < stages ? (s + ft) % stages : s) * KS;
+    const uint32_t oob = (uint32_t)(k0 + lc * 8 >= (uint32_t)K) << 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wreg[d][i] = buffer_load_16B(rW, (w_voff[i] + k0 * 2) | oob);
+  };
+  auto load_x = [&](int s, int d) __attribute__((always_inline)) {
+    const uint32_t k0 = (uint32_t)(s < stages ? (s + ft) % stages : s) * KS;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t k = k0 + kq * 64 + j * 16 + h * 8;
+      xreg[d][j] = buffer_load_16B(rX, (x_voff + (k0 + j * 16) * 2) | ((uint32_t)(k >= (uint32_t)K) << 31));
+    }
+  };
+  auto put = [&](int buf, int d) __attribute__((always_inline)) {
+    uint8_t* b = lds + buf * kBufBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(b + w_lds[i]) = wreg[d][i];
+  };
+  f32x16 acc = {};
+  auto compute = [&](int buf, int d) __attribute__((always_inline)) {
+    const uint8_t* b = lds + buf * kBufBytes;
+    bf16x8 wf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wf[j] = *reinterpret_cast<const bf16x8*>(b + f_lds[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], __builtin_bit_cast(bf16x8, xreg[d][j]), acc, 0, 0, 0);
+  };
+
+  // Step s handles the s-th stage of the rotated order. Stage s: its W sits in register slot
+  // s % DR and, once written, in LDS buffer s % 2; its X in slot s % DX. Step s: multiply stage s; write stage s + 1 to the other buffer (free:
+  // everyone passed the barrier after multiplying stage s - 1); load the W of stage s + DR
+  // and the X of stage s + DX into the slots stage s vacated. A stage past the last reads
+  // only zeros and adds nothing.
+#pragma unroll
+  for (int d = 0; d < DR; ++d) load_w(d, d);
+#pragma unroll
+  for (int d = 0; d < DX; ++d) load_x(d, d);
+  put(0, 0);
+  __syncthreads();
+  for (int s0 = 0; s0 < stages; s0 += DR) {
+#pragma unroll
+    for (int d = 0; d < DR; ++d) {
+      const int s = s0 + d;
+      compute(d & 1, d % DX);
+      put((d + 1) & 1, (d + 1) % DR);
+      load_w(s + DR, d);
+      load_x(s + DX, d % DX);
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  run_staged_epilogue<BF, 4, BT, 1>(a, reinterpret_cast<float*>(lds), t0, f0, min(BT, a.M - t0), tt, ft, slot,
+                                    s_amax, [&](int, float* tile) {
+                                      stage_block<BF>(tile + kq * BT * BF, acc, fb * 32, 0);
                                     });
 }
 
@@ -97,6 +155,7 @@ hipError_t launch_gemm_bf16_skinny(GemmArgs a, hipStream_t stream) {
 
 int gemm_bf16_skinny_tile_t() { return BT; }
 int gemm_bf16_skinny_tile_f() { return BF; }
+int gemm_bf16_skinny_threads() { return kThreads; }
 const void* gemm_bf16_skinny_symbol() { return reinterpret_cast<const void*>(&gemm_bf16_skinny_kernel); }
 
 }  // namespace fusedops

@@ -17,10 +17,11 @@ int gemm_bf16_t256_tile_f();
 const void* gemm_bf16_t256_symbol(const EpiParams& e);
 
 // bf16 GEMM + epilogue for few tokens (decode): 32-token x 64-feature tiles, K split
-// over the 4 waves.
+// over the 8 waves of a workgroup.
 hipError_t launch_gemm_bf16_skinny(GemmArgs a, hipStream_t stream);
 int gemm_bf16_skinny_tile_t();
 int gemm_bf16_skinny_tile_f();
+int gemm_bf16_skinny_threads();
 const void* gemm_bf16_skinny_symbol();
 
 // fp32 GEMM + epilogue (v_mfma_f32_32x32x2_f32), 64-token x 128-feature tiles.
