@@ -156,56 +156,74 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
 
   // One K step s from LDS buffer s&1: the MFMAs of the step, the fill of buffer (s+1)&1
   // from the stage set (data of step s+1), and the loads of step s+2 into the stage set.
-  // The fragment reads of sub-step kk+1 and the fills / loads are interleaved with
-  // sub-step kk's MFMAs. The last two steps fill and load past the end of K: those loads
-  // read zeros into a buffer that is not read again.
+  // The fills and loads are done in sub-steps 0..2 and the step's one barrier comes after
+  // sub-step 2: by then every wave has read its last fragments of buffer s&1 and written its
+  // part of buffer (s+1)&1. Sub-step 3's MFMAs then run while the first fragments of step
+  // s+1 are read, so no fragment read waits behind the barrier. The fragments of sub-step 0
+  // arrive from the previous step (or the prologue). The last two steps fill and load past
+  // the end of K: those loads read zeros into a buffer that is not read again.
   auto kstep = [&](int s) __attribute__((always_inline)) {
     const int CUR = s & 1;
-    read_frags(CUR, 0, fa[0], fb_[0]);
     // sub-step kk is a compile-time constant so every register array index is static
     auto sub = [&](auto kk_c) __attribute__((always_inline)) {
       constexpr int kk = decltype(kk_c)::value;
       // keep each sub-step's work together: at most one sub-step of fragments in flight
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kk < 3) read_frags(CUR, kk + 1, fa[(kk + 1) & 1], fb_[(kk + 1) & 1]);
+      else read_frags(CUR ^ 1, 0, fa[0], fb_[0]);
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][f], fb_[kk & 1][t], acc[f][t], 0, 0, 0);
-      store_q(CUR ^ 1, kk);
-      load_q((s + 2) * BK, kk);
+      // fills and loads: quarters 0 and 1 in sub-step 0, 2 in sub-step 1, 3 in sub-step 2
+      if constexpr (kk == 0) {
+        store_q(CUR ^ 1, 0);
+        store_q(CUR ^ 1, 1);
+        load_q((s + 2) * BK, 0);
+        load_q((s + 2) * BK, 1);
+      } else if constexpr (kk < 3) {
+        store_q(CUR ^ 1, kk + 1);
+        load_q((s + 2) * BK, kk + 1);
+      }
       // issue pattern per sub-step: MFMA / DS-read pairs, then MFMAs interleaved with the
       // fills and the global loads
-      if constexpr (kk < 3) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (kk == 0) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      } else if constexpr (kk < 3) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     };
     sub(std::integral_constant<int, 0>{});
     sub(std::integral_constant<int, 1>{});
     sub(std::integral_constant<int, 2>{});
-    sub(std::integral_constant<int, 3>{});
     __syncthreads();
+    sub(std::integral_constant<int, 3>{});
   };
 
   const int steps = (K + BK - 1) / BK;
-  // prologue: step 0 into LDS buffer 0, step 1 into the stage set
+  // prologue: step 0 into LDS buffer 0, step 1 into the stage set, step 0's first fragments
 #pragma unroll
   for (int q = 0; q < 4; ++q) load_q(0, q);
 #pragma unroll
@@ -214,9 +232,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   for (int q = 0; q < 4; ++q) load_q(BK, q);
   if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
   __syncthreads();
+  read_frags(0, 0, fa[0], fb_[0]);
 
 #pragma clang loop unroll(disable)
   for (int s = 0; s < steps; ++s) kstep(s);
+  __syncthreads();  // every wave's last fragment reads are done before LDS is reused
 
   if constexpr ((F & epi::kStatic) != 0) {
     // Epilogue on the accumulators in place; the mainloop's LDS buffers (128 KB) stage
