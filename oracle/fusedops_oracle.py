@@ -29,6 +29,9 @@ in the repository's design notes):
 * FP8 is OCP E4M3FN (max 448); s = fl32(absmax / 448); values are clamped to
   +-448 before round-to-nearest-even, so the encoder saturates, never NaN.
 * SwiGLU reads gate = column 2j and up = column 2j+1: y_j = silu(gate) * up.
+* FP8 inputs: one scale group spanning all of K, i.e. one activation scale per
+  row of X and one weight scale per row of W (output channel); both multiply the
+  fp32 accumulator before the bias, which stays a 16-bit float vector.
 """
 
 from __future__ import annotations
@@ -40,7 +43,7 @@ from scipy.special import erf as _erf
 
 __all__ = [
     "PARTIAL_COLS", "E4M3_MAX",
-    "contract", "gelu_erf", "gelu_tanh", "silu", "swiglu_pairs",
+    "contract", "dequant_contract", "gelu_erf", "gelu_tanh", "silu", "swiglu_pairs",
     "linear_epilogue", "rowsumsq_partials", "rmsnorm_finalize", "rmsnorm_apply",
     "layernorm_stats", "layernorm", "layernorm_gelu",
     "merge_sumsq", "merge_absmax", "merge_mean_m2", "merge_max_sumexp",
@@ -69,6 +72,23 @@ def contract(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     return x @ w.T
+
+
+def dequant_contract(xq: np.ndarray, wq: np.ndarray, x_scale=None, w_scale=None) -> np.ndarray:
+    """y[m,n] = sw[n] * sa[m] * sum_k xq[m,k] wq[n,k], the scale-after-accumulate form.
+
+    [Epilogue] §量化尾声的完整形态, "尾声里的量化权重反解与 per-group scale": the
+    accumulator keeps the unscaled partial sum over a group g of K and the epilogue
+    multiplies it by the weight scale of (n, g) and the activation scale of (m, g).
+    Here there is one group covering all of K. xq and wq are the decoded values of
+    the stored low-precision codes (fp64); a missing scale is 1.
+    """
+    h = contract(xq, wq)
+    if x_scale is not None:
+        h = h * np.asarray(x_scale, dtype=np.float64)[:, None]
+    if w_scale is not None:
+        h = h * np.asarray(w_scale, dtype=np.float64)[None, :]
+    return h
 
 
 def gelu_erf(h: np.ndarray) -> np.ndarray:
@@ -133,9 +153,11 @@ def rowsumsq_partials(h1: np.ndarray, partial_cols: int = PARTIAL_COLS) -> np.nd
 
 
 def linear_epilogue(x, w, bias=None, residual=None, col_scale=None, row_scale=None,
-                    act=None, partial_cols: int = PARTIAL_COLS) -> dict:
+                    act=None, partial_cols: int = PARTIAL_COLS, x_scale=None, w_scale=None) -> dict:
     """The fused linear layer and its epilogue chain, in its fixed order.
 
+    h  = sa[m] sw[n] (X W^T) + b                see dequant_contract (sa, sw only for
+                                                low-precision inputs; 1 otherwise)
     h  = X W^T + b                              [Fusion] §Linear算子剖析, Y_{m,n}
     h1 = h + z                                  [Epilogue] §模式A, Epilogue 1
     p  = row sum-of-squares partials of h1      [Epilogue] §模式A, partialRMS
@@ -146,7 +168,7 @@ def linear_epilogue(x, w, bias=None, residual=None, col_scale=None, row_scale=No
     Returns a dict with 'h1' (the value a STORE_AUX op writes), 'partials',
     and 'y' (the main output before any rounding or quantisation).
     """
-    h = contract(x, w)
+    h = dequant_contract(x, w, x_scale, w_scale)
     if bias is not None:
         h = h + np.asarray(bias, dtype=np.float64)[None, :]
     h1 = h if residual is None else h + np.asarray(residual, dtype=np.float64)

@@ -111,6 +111,74 @@ def _load_cdf():
     return rows
 
 
+# ---------------------------------------------------------------------------
+# low-precision inputs: scale-after-accumulate dequantisation
+# ---------------------------------------------------------------------------
+
+def _finite_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c ^ 0x01, c).astype(np.uint8)  # no NaN codes
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 3, 9), (2, 7, 4), (1, 1, 1)])
+def test_dequant_contract_brute_force(M, N, K):
+    # y[m][n] = sw[n] * sa[m] * sum_k xq[m][k] wq[n][k], written out element by element; M != N
+    # so an activation scale applied along the wrong axis cannot pass
+    rng = np.random.default_rng([21, M, N, K])
+    xq = O.e4m3_decode(_finite_codes(rng, (M, K)))
+    wq = O.e4m3_decode(_finite_codes(rng, (N, K)))
+    sa = rng.uniform(0.01, 2.0, size=M) * rng.choice([-1.0, 1.0], size=M)
+    sw = rng.uniform(0.01, 2.0, size=N)
+    ref = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += xq[m, k] * wq[n, k]
+            ref[m, n] = sw[n] * sa[m] * acc
+    np.testing.assert_allclose(O.dequant_contract(xq, wq, sa, sw), ref, rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(O.dequant_contract(xq, wq), O.contract(xq, wq), rtol=0, atol=0)
+
+
+def test_dequant_equals_dequantising_the_inputs_first():
+    # one scale group over all of K: scaling after the accumulation equals contracting the
+    # dequantised operands xq * sa[m] and wq * sw[n] (linearity)
+    rng = np.random.default_rng(22)
+    M, N, K = 6, 4, 33
+    xq = O.e4m3_decode(_finite_codes(rng, (M, K)))
+    wq = O.e4m3_decode(_finite_codes(rng, (N, K)))
+    sa = rng.uniform(0.001, 1.0, size=M)
+    sw = rng.uniform(0.001, 1.0, size=N)
+    direct = O.contract(xq * sa[:, None], wq * sw[:, None])
+    np.testing.assert_allclose(O.dequant_contract(xq, wq, sa, sw), direct, rtol=1e-12, atol=1e-12)
+
+
+def test_dequant_integer_codes_and_power_of_two_scales_exact():
+    # codes whose values are small integers and power-of-two scales: every result is exact
+    ints = np.array([-4.0, -3.0, -2.0, -1.0, 0.0, 1.0, 2.0, 3.0, 4.0])
+    codes = O.e4m3_encode(ints)
+    assert np.array_equal(O.e4m3_decode(codes), ints)
+    rng = np.random.default_rng(23)
+    xi = rng.integers(0, len(ints), size=(4, 16))
+    wi = rng.integers(0, len(ints), size=(3, 16))
+    xq, wq = O.e4m3_decode(codes[xi]), O.e4m3_decode(codes[wi])
+    sa = np.array([0.5, 2.0, 0.25, 8.0])
+    sw = np.array([4.0, 0.125, 1.0])
+    want = (ints[xi] @ ints[wi].T) * sa[:, None] * sw[None, :]
+    assert np.array_equal(O.dequant_contract(xq, wq, sa, sw), want)
+
+
+def test_fp8_input_worked_example_bias_is_not_scaled():
+    # x codes 0x38, 0x40 (1, 2); w codes 0x38, 0x38 (1, 1); sa = 0.5, sw = 2, b = 0.25:
+    # y = 0.5 * 2 * (1 + 2) + 0.25 = 3.25 (scaling the bias too would give 3.5)
+    xq = O.e4m3_decode(np.array([[0x38, 0x40]], dtype=np.uint8))
+    wq = O.e4m3_decode(np.array([[0x38, 0x38]], dtype=np.uint8))
+    out = O.linear_epilogue(xq, wq, bias=[0.25], x_scale=[0.5], w_scale=[2.0])
+    assert out["y"][0, 0] == 3.25
+    out = O.linear_epilogue(xq, wq, bias=[0.25], x_scale=[0.5], w_scale=[2.0], act="gelu_erf")
+    assert out["y"][0, 0] == pytest.approx(3.25 * 0.5 * (1.0 + math.erf(3.25 / math.sqrt(2.0))), rel=1e-15)
+
+
 def test_gelu_erf_textbook_normal_cdf():
     for x, phi in _load_cdf():
         assert O.gelu_erf(np.array([x]))[0] == pytest.approx(x * phi, rel=1e-15, abs=1e-16)
