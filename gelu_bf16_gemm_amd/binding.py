@@ -33,7 +33,7 @@ lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 F32, BF16, F16, F8E4M3 = 0, 1, 2, 3
 (OP_RESIDUAL_ADD, OP_STORE_AUX, OP_ROWSUMSQ_PARTIAL, OP_COL_SCALE, OP_ROW_SCALE, OP_GELU_ERF,
- OP_GELU_TANH, OP_SWIGLU, OP_QUANT_FP8_ROW, OP_SPLIT_COLS) = range(1, 11)
+ OP_GELU_TANH, OP_SWIGLU, OP_QUANT_FP8_ROW, OP_SPLIT_COLS, OP_DEQUANT_ROW, OP_DEQUANT_COL) = range(1, 13)
 GELU_NONE, GELU_TANH, GELU_ERF = 0, 1, 2
 PARTIAL_COLS = 128
 LN_MAX_COLS = 16384

@@ -19,6 +19,7 @@ LIB = os.path.join(PKG, "libfusedops.so")
 SOURCES = [
     "gemm_bf16.hip",
     "gemm_bf16_skinny.hip",
+    "gemm_fp8.hip",
     "gemm_f32.hip",
     "layernorm_gelu.hip",
     "rmsnorm_finalize.hip",

@@ -52,7 +52,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Parsed epilogue op list.
 struct OpList {
-  const fusedops_op* by_kind[11] = {};
+  const fusedops_op* by_kind[13] = {};
   int act = ACT_NONE;
   bool quant = false;
 };
@@ -63,8 +63,8 @@ int32_t parse_ops(const fusedops_op* ops, int32_t n_ops, OpList& out) {
   int n_act = 0;
   for (int i = 0; i < n_ops; ++i) {
     const fusedops_op& op = ops[i];
-    if (op.kind < FUSEDOPS_OP_RESIDUAL_ADD || op.kind > FUSEDOPS_OP_SPLIT_COLS) return FUSEDOPS_ERR_INVALID_ARG;
-    if (op.kind <= last) return FUSEDOPS_ERR_INVALID_ARG;  // canonical order, each kind once
+    if (op.kind < FUSEDOPS_OP_RESIDUAL_ADD || op.kind > FUSEDOPS_OP_DEQUANT_COL) return FUSEDOPS_ERR_INVALID_ARG;
+    if (op.kind <= last) return FUSEDOPS_ERR_INVALID_ARG;  // increasing kind order, each kind once
     if (op.reserved != 0) return FUSEDOPS_ERR_INVALID_ARG;
     last = op.kind;
     out.by_kind[op.kind] = &op;
@@ -91,7 +91,7 @@ size_t ws_bytes_for(int64_t M, int64_t N) {
   return (size_t)(cdiv(words * 4, 256) * 256);
 }
 
-enum class Kernel { T256, SKINNY, F32 };
+enum class Kernel { T256, SKINNY, F32, FP8 };
 
 // Map a launch result to a status; with FUSEDOPS_VERBOSE set, name the refused launch on stderr.
 int32_t launch_status(hipError_t err, const char* what) {
@@ -138,7 +138,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (!X || !W) return FUSEDOPS_ERR_INVALID_ARG;
   if (M < 1 || N < 1 || K < 1) return FUSEDOPS_ERR_INVALID_ARG;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return FUSEDOPS_ERR_INVALID_ARG;
-  if (in_dtype != FUSEDOPS_BF16 && in_dtype != FUSEDOPS_F32) return FUSEDOPS_ERR_UNSUPPORTED;
+  if (in_dtype == FUSEDOPS_F16) return FUSEDOPS_ERR_UNSUPPORTED;
   if (M > (1 << 30) || N > (1 << 30) || K > (1 << 30)) return FUSEDOPS_ERR_UNSUPPORTED;
   OpList ol;
   if (int32_t st = parse_ops(ops, n_ops, ol)) return st;
@@ -149,10 +149,14 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   const fusedops_op* op_row = ol.by_kind[FUSEDOPS_OP_ROW_SCALE];
   const fusedops_op* op_q = ol.by_kind[FUSEDOPS_OP_QUANT_FP8_ROW];
   const fusedops_op* op_split = ol.by_kind[FUSEDOPS_OP_SPLIT_COLS];
+  const fusedops_op* op_dqr = ol.by_kind[FUSEDOPS_OP_DEQUANT_ROW];
+  const fusedops_op* op_dqc = ol.by_kind[FUSEDOPS_OP_DEQUANT_COL];
+  const bool fp8_in = in_dtype == FUSEDOPS_F8E4M3;
   const bool swiglu = ol.act == ACT_SWIGLU;
   const int64_t n_out = swiglu ? N / 2 : N;
   const int64_t T = cdiv(N, FUSEDOPS_PARTIAL_COLS);
   const int es_in = dtype_size(in_dtype);
+  const int bias_dtype = fp8_in ? FUSEDOPS_BF16 : in_dtype;  // FP8 inputs take a bf16 bias
 
   // ---- output dtype rules
   if (ol.quant) {
@@ -179,6 +183,8 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (op_gam && (!op_gam->in || !float_dtype(op_gam->dtype))) return FUSEDOPS_ERR_INVALID_ARG;
   if (op_row && !op_row->in) return FUSEDOPS_ERR_INVALID_ARG;
   if (op_q && !op_q->out) return FUSEDOPS_ERR_INVALID_ARG;
+  if ((op_dqr || op_dqc) && !fp8_in) return FUSEDOPS_ERR_INVALID_ARG;  // scales of FP8 inputs only
+  if ((op_dqr && !op_dqr->in) || (op_dqc && !op_dqc->in)) return FUSEDOPS_ERR_INVALID_ARG;
   if (swiglu && (N % 2)) return FUSEDOPS_ERR_INVALID_ARG;
   if (ldx < K || ldw < K) return FUSEDOPS_ERR_INVALID_ARG;
   if (Y && ldy < n_out) return FUSEDOPS_ERR_INVALID_ARG;
@@ -196,6 +202,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (op_gam && !aligned(op_gam->in, 16)) return FUSEDOPS_ERR_MISALIGNED;
   if (op_row && !aligned(op_row->in, 4)) return FUSEDOPS_ERR_MISALIGNED;
   if (op_q && !aligned(op_q->out, 4)) return FUSEDOPS_ERR_MISALIGNED;
+  if ((op_dqr && !aligned(op_dqr->in, 4)) || (op_dqc && !aligned(op_dqc->in, 4))) return FUSEDOPS_ERR_MISALIGNED;
   if (op_split) {
     if ((N / op_split->n_split) % 8) return FUSEDOPS_ERR_MISALIGNED;
     if ((op_split->ld * es_out) % 16) return FUSEDOPS_ERR_MISALIGNED;
@@ -204,11 +211,14 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   }
 
   // ---- aliasing: outputs may not overlap inputs or each other, except Y == z exactly
-  Span in_spans[6] = {
-      span2d(X, M, K, ldx, es_in), span2d(W, N, K, ldw, es_in), span2d(bias, 1, N, N, es_in),
+  constexpr int kInSpans = 8;
+  Span in_spans[kInSpans] = {
+      span2d(X, M, K, ldx, es_in), span2d(W, N, K, ldw, es_in), span2d(bias, 1, N, N, dtype_size(bias_dtype)),
       op_res ? span2d(op_res->in, M, N, op_res->ld, dtype_size(op_res->dtype)) : Span{},
       op_gam ? span2d(op_gam->in, 1, N, N, dtype_size(op_gam->dtype)) : Span{},
-      op_row ? span2d(op_row->in, 1, M, M, 4) : Span{}};
+      op_row ? span2d(op_row->in, 1, M, M, 4) : Span{},
+      op_dqr ? span2d(op_dqr->in, 1, M, M, 4) : Span{},
+      op_dqc ? span2d(op_dqc->in, 1, N, N, 4) : Span{}};
   Span out_spans[6];
   int n_out_spans = 0;
   if (Y) out_spans[n_out_spans++] = span2d(Y, M, n_out, ldy, es_out);
@@ -221,7 +231,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   const bool y_is_z = Y && op_res && Y == op_res->in && ldy == op_res->ld && out_dtype == op_res->dtype &&
                       !swiglu;
   for (int o = 0; o < n_out_spans; ++o) {
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < kInSpans; ++i) {
       if (!overlap(out_spans[o], in_spans[i])) continue;
       if (y_is_z && o == 0 && i == 3) continue;
       return FUSEDOPS_ERR_INVALID_ARG;
@@ -237,7 +247,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
                   reinterpret_cast<uintptr_t>(workspace) + workspace_bytes, true};
     for (int o = 0; o < n_out_spans; ++o)
       if (overlap(sw, out_spans[o])) return FUSEDOPS_ERR_INVALID_ARG;
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < kInSpans; ++i)
       if (overlap(sw, in_spans[i])) return FUSEDOPS_ERR_INVALID_ARG;
   }
 
@@ -245,18 +255,21 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   Kernel kern;
   if (in_dtype == FUSEDOPS_F32) {
     kern = Kernel::F32;
+  } else if (fp8_in) {
+    kern = Kernel::FP8;
   } else {
     const int64_t big_tiles = cdiv(M, 256) * cdiv(N, 256);
     kern = (M <= 128 && !op_par && big_tiles < 256) ? Kernel::SKINNY : Kernel::T256;
   }
-  const int tile_rows = kern == Kernel::T256 ? 256 : (kern == Kernel::SKINNY ? 64 : 128);
-  const int tile_tok = kern == Kernel::T256 ? 256 : (kern == Kernel::SKINNY ? 32 : 64);
+  const bool big = kern == Kernel::T256 || kern == Kernel::FP8;  // the 256 x 256 tile kernels
+  const int tile_rows = big ? 256 : (kern == Kernel::SKINNY ? 64 : 128);
+  const int tile_tok = big ? 256 : (kern == Kernel::SKINNY ? 32 : 64);
   // 32-bit buffer offsets cover one tile's rows (operands, and the residual rows the
   // 256 x 256 kernel copies into LDS)
   if (((int64_t)(tile_rows - 1) * ldw + K) * es_in >= (int64_t(1) << 31) ||
       ((int64_t)(tile_tok - 1) * ldx + K) * es_in >= (int64_t(1) << 31))
     return FUSEDOPS_ERR_UNSUPPORTED;
-  if (op_res && kern == Kernel::T256 &&
+  if (op_res && big &&
       ((int64_t)(tile_tok - 1) * op_res->ld + 256) * dtype_size(op_res->dtype) >= (int64_t(1) << 31))
     return FUSEDOPS_ERR_UNSUPPORTED;
 
@@ -265,7 +278,9 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   a.X = X; a.ldx = ldx; a.W = W; a.ldw = ldw;
   a.M = (int)M; a.N = (int)N; a.K = (int)K;
   EpiParams& e = a.ep;
-  e.bias = bias; e.bias_dtype = in_dtype;
+  e.bias = bias; e.bias_dtype = bias_dtype;
+  if (op_dqr) e.dq_row = static_cast<const float*>(op_dqr->in);
+  if (op_dqc) e.dq_col = static_cast<const float*>(op_dqc->in);
   if (op_res) { e.z = op_res->in; e.ldz = op_res->ld; e.z_dtype = op_res->dtype; }
   if (op_aux) { e.aux = op_aux->out; e.ld_aux = op_aux->ld; e.aux_dtype = op_aux->dtype; }
   if (op_par) { e.partials = static_cast<float*>(op_par->out); e.ldp = op_par->ld; }
@@ -294,8 +309,10 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   // at the same time: check the device can hold that many workgroups at once.
   if (ol.quant) {
     const int tile_f = kern == Kernel::T256 ? gemm_bf16_t256_tile_f()
+                       : kern == Kernel::FP8 ? gemm_fp8_t256_tile_f()
                        : kern == Kernel::SKINNY ? gemm_bf16_skinny_tile_f() : gemm_f32_tile_f();
     const void* sym = kern == Kernel::T256 ? gemm_bf16_t256_symbol(a.ep)
+                      : kern == Kernel::FP8 ? gemm_fp8_t256_symbol(a.ep)
                       : kern == Kernel::SKINNY ? gemm_bf16_skinny_symbol() : gemm_f32_symbol();
     const int threads = kern == Kernel::SKINNY ? gemm_bf16_skinny_threads() : 256;
     int dev = 0, cus = 0, per_cu = 0;
@@ -313,6 +330,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   switch (kern) {
     case Kernel::T256: return launch_status(launch_gemm_bf16_t256(a, s), "gemm_bf16_t256");
     case Kernel::SKINNY: return launch_status(launch_gemm_bf16_skinny(a, s), "gemm_bf16_skinny");
+    case Kernel::FP8: return launch_status(launch_gemm_fp8_t256(a, s), "gemm_fp8_t256");
     default: return launch_status(launch_gemm_f32(a, s), "gemm_f32");
   }
 }

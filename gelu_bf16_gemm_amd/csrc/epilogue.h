@@ -32,6 +32,8 @@ struct EpiParams {
   float* partials;        int64_t ldp;
   const void* gamma;      int gamma_dtype;
   const float* rscale;
+  const float* dq_row;    // FP8 inputs: activation scale per row of X (null: 1)
+  const float* dq_col;    // FP8 inputs: weight scale per output channel (null: 1)
   int act;
   int quant;              // FP8 per-row quantised writeback
   float* scales;

@@ -19,44 +19,21 @@
 
 #include "acc_epilogue.h"
 #include "kernels.h"
+#include "tile256.h"
 
 namespace fusedops {
 
 namespace {
+
+using t256::lds_off;
+using t256::swz;
+using t256::tile_coords;
 
 constexpr int BF = 256;   // features per tile
 constexpr int BT = 256;   // tokens per tile
 constexpr int BK = 64;    // K per step
 constexpr int kThreads = 256;
 constexpr int kTileBytes = 256 * BK * 2;  // one operand tile in LDS (32 KB)
-
-// 16-byte chunk `chunk` of LDS row `row` sits at chunk position chunk ^ f(row) with
-// f(row) = (row & 7) ^ ((row >> 3) & 1): any 8 consecutive rows at one logical chunk use 8
-// distinct positions (128-byte bank window) and any 16 consecutive rows use 16 distinct
-// (position, row parity) pairs (256-byte bank window), for reads and fills alike.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ swz(row)) << 4));
-}
-
-// Map a linear tile id to (token tile, feature tile). Consecutive workgroups are
-// dealt round-robin to the 8 XCDs; regroup so that each XCD walks a contiguous
-// range of tile ids, and within that range cover GROUP_T token tiles x all
-// feature tiles so concurrently running tiles share operand rows in the XCD's L2.
-__device__ __forceinline__ void tile_coords(int pid, int tiles_t, int tiles_f, int& tt, int& ft) {
-  const int G = tiles_t * tiles_f;
-  const int xcd = pid & 7, local = pid >> 3;
-  const int base = G >> 3, rem = G & 7;
-  const int p2 = xcd * base + min(xcd, rem) + local;
-  constexpr int GROUP_T = 4;
-  const int group_size = GROUP_T * tiles_f;
-  const int g = p2 / group_size;
-  const int first_t = g * GROUP_T;
-  const int gt = min(tiles_t - first_t, GROUP_T);
-  const int in = p2 - g * group_size;
-  tt = first_t + in % gt;
-  ft = in / gt;
-}
 
 template <uint32_t F>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a) {

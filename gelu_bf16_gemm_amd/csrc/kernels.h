@@ -16,6 +16,12 @@ int gemm_bf16_t256_tile_t();
 int gemm_bf16_t256_tile_f();
 const void* gemm_bf16_t256_symbol(const EpiParams& e);
 
+// E4M3 inputs, 256 x 256 tiles (any M): v_mfma_scale_f32_32x32x64_f8f6f4 mainloop, the
+// dequantisation scales applied to the accumulators, then the same epilogues as above
+hipError_t launch_gemm_fp8_t256(GemmArgs a, hipStream_t stream);
+int gemm_fp8_t256_tile_f();
+const void* gemm_fp8_t256_symbol(const EpiParams& e);
+
 // bf16 GEMM + epilogue for few tokens (decode): 32-token x 64-feature tiles, K split
 // over the 8 waves of a workgroup.
 hipError_t launch_gemm_bf16_skinny(GemmArgs a, hipStream_t stream);

@@ -113,10 +113,28 @@ WORKLOADS = {
     "prefill_swiglu_fp8_bf16_16384x16384x2048": dict(config_id=9, kind="linear", M=16384, N=16384,
                                                      K=2048, in_dtype=BF16, bias=False, act="swiglu",
                                                      quant_fp8=True, out_dtype=F8E4M3),
+    # E4M3 inputs with per-row activation and per-channel weight scales: the down-projection
+    # that consumes the quantised SwiGLU output above, with its residual add.
+    "downproj_residual_fp8in_16384x2048x8192": dict(config_id=10, kind="linear", M=16384, N=2048,
+                                                    K=8192, in_dtype=F8E4M3, bias=False, act=None,
+                                                    residual=True, dequant=True, out_dtype=BF16),
+    # The MLP-up layer of config 5 with E4M3 inputs (bias bf16).
+    "mlp_up_gelu_fp8in_8192x16384x4096": dict(config_id=11, kind="linear", M=8192, N=16384, K=4096,
+                                              in_dtype=F8E4M3, bias=True, act="gelu_erf",
+                                              dequant=True, out_dtype=BF16),
 }
 
 # tensor ids inside one config
-_T_X, _T_W, _T_B, _T_Z, _T_GAMMA, _T_BETA = 0, 1, 2, 3, 4, 5
+_T_X, _T_W, _T_B, _T_Z, _T_GAMMA, _T_BETA, _T_SA, _T_SW = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+def random_e4m3_codes(rng: np.random.Generator, shape, e_lo: int = 4, e_hi: int = 10) -> np.ndarray:
+    """Random OCP E4M3 bit patterns: uniform sign, exponent field uniform in [e_lo, e_hi], uniform
+    3-bit mantissa (magnitudes 2^(e_lo-7) .. 1.875 * 2^(e_hi-7); never NaN)."""
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    exp = rng.integers(e_lo, e_hi + 1, size=shape, dtype=np.uint8) << 3
+    man = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    return (sign | exp | man).astype(np.uint8)
 
 
 def make_linear_inputs(spec: dict, seed: int = 0, M: int | None = None, N: int | None = None,
@@ -132,15 +150,23 @@ def make_linear_inputs(spec: dict, seed: int = 0, M: int | None = None, N: int |
     K = spec["K"] if K is None else K
     dt = spec["in_dtype"]
     out = {"M": M, "N": N, "K": K, "in_dtype": dt}
-    out["X"] = store(normal(rng_for(cid, _T_X, seed), (M, K)), dt)
-    out["W"] = store(normal(rng_for(cid, _T_W, seed), (N, K), std=float(1.0 / np.sqrt(K))), dt)
+    vec_dt = dt if dt == F32 else BF16  # bias, residual and gamma of 16-bit and E4M3 layers are bf16
+    if dt == F8E4M3:
+        # codes of magnitude 1/8 .. 15 with scales around 1/8 (activations) and 1/(8 sqrt K)
+        # (weights): dequantised X is O(1) and W about N(0, 1/K) in size
+        out["X"] = random_e4m3_codes(rng_for(cid, _T_X, seed), (M, K))
+        out["W"] = random_e4m3_codes(rng_for(cid, _T_W, seed), (N, K))
+        out["sa"] = (rng_for(cid, _T_SA, seed).uniform(0.5, 1.5, size=M) / 8.0).astype(np.float32)
+        out["sw"] = (rng_for(cid, _T_SW, seed).uniform(0.5, 1.5, size=N) / (8.0 * np.sqrt(K))).astype(np.float32)
+    else:
+        out["X"] = store(normal(rng_for(cid, _T_X, seed), (M, K)), dt)
+        out["W"] = store(normal(rng_for(cid, _T_W, seed), (N, K), std=float(1.0 / np.sqrt(K))), dt)
     if spec.get("bias"):
-        out["b"] = store(normal(rng_for(cid, _T_B, seed), (N,), std=0.02), dt)
+        out["b"] = store(normal(rng_for(cid, _T_B, seed), (N,), std=0.02), vec_dt)
     if spec.get("residual"):
-        out["z"] = store(normal(rng_for(cid, _T_Z, seed), (M, N)), BF16 if dt == BF16 else dt)
+        out["z"] = store(normal(rng_for(cid, _T_Z, seed), (M, N)), vec_dt)
     if spec.get("col_scale"):
-        out["gamma"] = store(normal(rng_for(cid, _T_GAMMA, seed), (N,), mean=1.0, std=0.1),
-                             BF16 if dt == BF16 else dt)
+        out["gamma"] = store(normal(rng_for(cid, _T_GAMMA, seed), (N,), mean=1.0, std=0.1), vec_dt)
     return out
 
 

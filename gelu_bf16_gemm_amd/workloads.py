@@ -42,7 +42,10 @@ class LinearRun:
         self.copies = copies
         self.X = [to_device(inp["X"], dt) for _ in range(copies)]
         self.W = [to_device(inp["W"], dt) for _ in range(copies)]
-        self.b = to_device(inp["b"], dt) if "b" in inp else None
+        vec_dt = dt if dt == I.F32 else I.BF16
+        self.b = to_device(inp["b"], vec_dt) if "b" in inp else None
+        self.sa = to_device(inp["sa"], I.F32) if "sa" in inp else None
+        self.sw = to_device(inp["sw"], I.F32) if "sw" in inp else None
         self.z = [to_device(inp["z"], I.BF16) for _ in range(copies)] if "z" in inp else None
         self.gamma = to_device(inp["gamma"], I.BF16) if "gamma" in inp else None
         act = spec.get("act")
@@ -91,6 +94,10 @@ class LinearRun:
             ops.append(B.op(B.OP_QUANT_FP8_ROW, out=self.scales))
         if self.split is not None:
             ops.append(B.op(B.OP_SPLIT_COLS, split=self.split))
+        if self.sa is not None:
+            ops.append(B.op(B.OP_DEQUANT_ROW, self.sa))
+        if self.sw is not None:
+            ops.append(B.op(B.OP_DEQUANT_COL, self.sw))
         return ops
 
     def launch(self, i: int = 0, stream=None) -> None:
@@ -131,11 +138,15 @@ class LinearRun:
     def bytes(self) -> float:
         """HBM bytes the method must move: each input once, each output once."""
         s, M, N, K = self.spec, self.M, self.N, self.K
-        es_in = 4 if s["in_dtype"] == I.F32 else 2
+        es_in = {I.F32: 4, I.BF16: 2, I.F16: 2, I.F8E4M3: 1}[s["in_dtype"]]
         es_out = {I.F32: 4, I.BF16: 2, I.F16: 2, I.F8E4M3: 1}[self.out_dtype]
         b = (M * K + N * K) * es_in + M * self.n_out * es_out
         if self.b is not None:
-            b += N * es_in
+            b += N * self.b.element_size()
+        if self.sa is not None:
+            b += M * 4
+        if self.sw is not None:
+            b += N * 4
         if self.z is not None:
             b += M * N * 2
         if self.aux is not None:

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define FUSEDOPS_ABI_VERSION 1
+#define FUSEDOPS_ABI_VERSION 2
 /* Width of one RMSNorm row partial: p[m,t] covers columns [128 t, 128 t + 128). */
 #define FUSEDOPS_PARTIAL_COLS 128
 /* Largest LayerNorm row supported by fusedops_layernorm_gelu (elements). */
@@ -59,10 +59,13 @@ enum fusedops_dtype {
 };
 
 /*
- * Epilogue op kinds. An op list must be given in this (canonical) order, each
- * kind at most once, and at most one of GELU_ERF / GELU_TANH / SWIGLU. With
- * acc = X W^T the chain is, per output element (m, n):
+ * Epilogue op kinds. An op list is given in increasing kind value, each kind at
+ * most once, and with at most one of GELU_ERF / GELU_TANH / SWIGLU. With
+ * acc = X W^T the chain is, per output element (m, n) (the two DEQUANT kinds,
+ * listed last, act first):
  *
+ *   acc = acc * sa[m] * sw[n]           DEQUANT_ROW (sa), DEQUANT_COL (sw); FP8 inputs only
+ *                                       [Epilogue] §量化尾声的完整形态 (per-group scales, one group)
  *   h  = acc + b[n]                     bias, when `bias` != NULL   [Fusion] §Linear算子剖析 Y_{m,n}
  *   h1 = h + z[m,n]                     RESIDUAL_ADD                [Epilogue] §模式A, Epilogue 1
  *        STORE_AUX writes h1            (rank-2 tile store)         [Epilogue] §六类尾声原语 item 4
@@ -93,6 +96,11 @@ enum fusedops_dtype {
  *   SPLIT_COLS        out_v[0..n_split-1] = destination blocks, n_split in {2, 3}, ld = row stride
  *                     of each block. Block i receives output columns [i d, (i+1) d), d = N / n_split
  *                     (Q, K, V order for n_split = 3). Y must be NULL. Not combinable with SWIGLU.
+ *   DEQUANT_ROW       in = sa (fp32, length M): the activation scale of each row of X, i.e. X holds
+ *                     E4M3 codes of x / sa[m] (as QUANT_FP8_ROW writes them). Requires in_dtype =
+ *                     F8E4M3. Absent: sa = 1.
+ *   DEQUANT_COL       in = sw (fp32, length N): the weight scale of each output channel (row of W).
+ *                     Requires in_dtype = F8E4M3. Absent: sw = 1.
  */
 enum fusedops_op_kind {
   FUSEDOPS_OP_RESIDUAL_ADD = 1,
@@ -104,7 +112,9 @@ enum fusedops_op_kind {
   FUSEDOPS_OP_GELU_TANH = 7,
   FUSEDOPS_OP_SWIGLU = 8,
   FUSEDOPS_OP_QUANT_FP8_ROW = 9,
-  FUSEDOPS_OP_SPLIT_COLS = 10
+  FUSEDOPS_OP_SPLIT_COLS = 10,
+  FUSEDOPS_OP_DEQUANT_ROW = 11,
+  FUSEDOPS_OP_DEQUANT_COL = 12
 };
 
 enum fusedops_gelu_form {
@@ -132,10 +142,11 @@ typedef struct fusedops_op {
  * row n = output neuron) and [Epilogue] §主循环与尾声 (the epilogue transforms each finished output
  * tile in registers before it is written back; see the op kinds above).
  *
- *   X      M x K, row stride ldx, dtype in_dtype (BF16, or F32 for the fp32 path).
+ *   X      M x K, row stride ldx, dtype in_dtype: BF16, F32 (the fp32 path) or F8E4M3 (codes;
+ *          the MFMA contraction runs on E4M3 operands with fp32 accumulation).
  *   W      N x K, row stride ldw, dtype in_dtype.
- *   bias   length N, dtype in_dtype, or NULL for no bias.
- *   M,N,K  >= 1. K must be a multiple of 8 (BF16) or 4 (F32); N a multiple of 8.
+ *   bias   length N, dtype in_dtype (BF16 when in_dtype is F8E4M3), or NULL for no bias.
+ *   M,N,K  >= 1. K must be a multiple of 8 (BF16), 4 (F32) or 16 (F8E4M3); N a multiple of 8.
  *   ops    n_ops ops in canonical order (n_ops = 0 allowed; ops may be NULL then).
  *   Y      M x N_out (N_out = N/2 with SWIGLU, else N), row stride ldy, dtype out_dtype
  *          in {BF16, F16, F32}, or F8E4M3 exactly when QUANT_FP8_ROW is present.

@@ -32,14 +32,14 @@ def test_header_symbols_are_exported():
 
 
 def test_constants():
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
     assert B.partial_cols() == 128
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
     assert B.status_string(0) == "ok"
     text = open(HEADER).read()
     assert "#define FUSEDOPS_PARTIAL_COLS 128" in text
-    assert "#define FUSEDOPS_ABI_VERSION 1" in text
+    assert "#define FUSEDOPS_ABI_VERSION 2" in text
 
 
 def lin(X=addr(0), ldx=64, W=addr(1), ldw=64, bias=None, M=32, N=64, K=64, in_dt=B.BF16, ops=(),
@@ -79,9 +79,23 @@ def test_linear_invalid_arguments():
 
 def test_linear_unsupported():
     assert lin(in_dt=B.F16) == B.ERR_UNSUPPORTED
-    assert lin(in_dt=B.F8E4M3) == B.ERR_UNSUPPORTED
     split = mkop(B.OP_SPLIT_COLS, out_v=[addr(3), addr(4)], n_split=2, ld=16)
     assert lin(ops=[mkop(B.OP_SWIGLU), split], Y=None) == B.ERR_UNSUPPORTED
+
+
+def test_fp8_input_rules():
+    # every case is refused before any launch (the addresses are placeholders)
+    row = mkop(B.OP_DEQUANT_ROW, dtype=B.F32, inp=addr(5))
+    col = mkop(B.OP_DEQUANT_COL, dtype=B.F32, inp=addr(6))
+    assert lin(in_dt=B.F8E4M3, K=8, ldx=64, ldw=64) == B.ERR_MISALIGNED        # K multiple of 16
+    assert lin(in_dt=B.F8E4M3, K=64, ldx=72, ldw=64, ops=[row, col]) == B.ERR_MISALIGNED  # 72-byte rows
+    assert lin(in_dt=B.BF16, ops=[row]) == B.ERR_INVALID_ARG                     # scales of FP8 inputs only
+    assert lin(in_dt=B.BF16, ops=[col]) == B.ERR_INVALID_ARG
+    assert lin(in_dt=B.F8E4M3, ops=[mkop(B.OP_DEQUANT_ROW, dtype=B.F32)]) == B.ERR_INVALID_ARG  # no input
+    assert lin(in_dt=B.F8E4M3, ops=[col, row]) == B.ERR_INVALID_ARG              # kind order
+    assert lin(in_dt=B.F8E4M3, ops=[mkop(B.OP_DEQUANT_ROW, dtype=B.F32, inp=addr(2))]) == B.ERR_INVALID_ARG  # aliases Y
+    assert lin(in_dt=B.F8E4M3, ldx=32, ops=[row, col]) == B.ERR_INVALID_ARG      # ldx < K
+    assert lin(in_dt=B.F8E4M3, ops=[mkop(B.OP_DEQUANT_ROW, dtype=B.F32, inp=addr(5) + 2)]) == B.ERR_MISALIGNED
 
 
 def test_op_list_rules():
@@ -92,7 +106,7 @@ def test_op_list_rules():
     assert lin(ops=[gelu, tanh]) == B.ERR_INVALID_ARG         # two activations
     assert lin(ops=[gelu, sw]) == B.ERR_INVALID_ARG
     assert lin(ops=[mkop(0)]) == B.ERR_INVALID_ARG            # unknown kind
-    assert lin(ops=[mkop(11)]) == B.ERR_INVALID_ARG
+    assert lin(ops=[mkop(13)]) == B.ERR_INVALID_ARG
     assert lin(ops=[mkop(B.OP_GELU_ERF, reserved=1)]) == B.ERR_INVALID_ARG
     assert lin(ops=[mkop(B.OP_RESIDUAL_ADD, ld=64)]) == B.ERR_INVALID_ARG      # no input
     assert lin(ops=[mkop(B.OP_RESIDUAL_ADD, inp=addr(5), ld=8)]) == B.ERR_INVALID_ARG  # ld < N

@@ -38,12 +38,16 @@ def test_linear_workload_full_size(name):
     M = spec["M"]
     rows = sample_rows(M)
     dt = spec["in_dtype"]
-    X = I.to_f64(inp["X"][rows], dt)
-    W = I.to_f64(inp["W"], dt)
-    ref = O.linear_epilogue(X, W, bias=I.to_f64(inp["b"], dt) if "b" in inp else None,
+    fp8 = dt == I.F8E4M3
+    X = O.e4m3_decode(inp["X"][rows]) if fp8 else I.to_f64(inp["X"][rows], dt)
+    W = O.e4m3_decode(inp["W"]) if fp8 else I.to_f64(inp["W"], dt)
+    vec_dt = I.BF16 if fp8 else dt
+    ref = O.linear_epilogue(X, W, bias=I.to_f64(inp["b"], vec_dt) if "b" in inp else None,
                             residual=I.to_f64(inp["z"][rows], I.BF16) if "z" in inp else None,
                             col_scale=I.to_f64(inp["gamma"], I.BF16) if "gamma" in inp else None,
-                            act=spec.get("act"))
+                            act=spec.get("act"),
+                            x_scale=inp["sa"][rows].astype(np.float64) if "sa" in inp else None,
+                            w_scale=inp["sw"].astype(np.float64) if "sw" in inp else None)
     out = run.outputs(rows)
     if spec.get("quant_fp8"):
         s = out["scales"].astype(np.float32)

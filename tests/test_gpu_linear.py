@@ -14,7 +14,8 @@ import torch
 import oracle as O
 from gelu_bf16_gemm_amd import inputs as I
 
-from helpers import workspace_ok, Guarded, check_f32, check_fp8, check_lowp, check_out, dev, host64, note
+from helpers import (workspace_ok, Guarded, check_f32, check_f32_e4m3_acc, check_fp8, check_lowp, check_out, dev,
+                     host64, note)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,22 +39,32 @@ def upload_padded(stored, dtype, pad):
 
 def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=None, residual=False,
                aux=False, partials=False, gamma=False, rscale=False, split=0, quant=False, seed=0,
-               pad=0, inplace=False, aux_dtype=None, z_dtype=None, check=True):
+               pad=0, inplace=False, aux_dtype=None, z_dtype=None, dq_row=True, dq_col=True, check=True):
     rng = np.random.default_rng([101, M, N, K, seed])
-    X = I.random_stored(rng, (M, K), in_dtype)
-    W = I.random_stored(rng, (N, K), in_dtype, std=1 / math.sqrt(K))
-    b = I.random_stored(rng, (N,), in_dtype, std=0.5) if bias else None
-    zdt = z_dtype if z_dtype is not None else (I.BF16 if in_dtype == I.BF16 else in_dtype)
+    fp8 = in_dtype == I.F8E4M3
+    sa = sw = None
+    if fp8:
+        # E4M3 codes with activation / weight scales (scale-after-accumulate inputs)
+        X = I.random_e4m3_codes(rng, (M, K))
+        W = I.random_e4m3_codes(rng, (N, K))
+        sa = (rng.uniform(0.5, 1.5, M) / 8.0).astype(np.float32) if dq_row else None
+        sw = (rng.uniform(0.5, 1.5, N) / (8.0 * math.sqrt(K))).astype(np.float32) if dq_col else None
+    else:
+        X = I.random_stored(rng, (M, K), in_dtype)
+        W = I.random_stored(rng, (N, K), in_dtype, std=1 / math.sqrt(K))
+    vec_dt = I.BF16 if fp8 else in_dtype  # the bias of E4M3 inputs is bf16
+    b = I.random_stored(rng, (N,), vec_dt, std=0.5) if bias else None
+    zdt = z_dtype if z_dtype is not None else (I.BF16 if in_dtype in (I.BF16, I.F8E4M3) else in_dtype)
     z = I.random_stored(rng, (M, N), zdt) if residual else None
     g = I.random_stored(rng, (N,), zdt, mean=1.0, std=0.1) if gamma else None
     r = rng.uniform(0.5, 1.5, M).astype(np.float32) if rscale else None
 
     note(f"linear M={M} N={N} K={K} in={in_dtype} out={out_dtype} act={act} bias={bias} res={residual} "
          f"aux={aux} partials={partials} gamma={gamma} rscale={rscale} split={split} quant={quant} "
-         f"pad={pad} inplace={inplace} seed={seed}")
+         f"pad={pad} inplace={inplace} seed={seed} dq=({sa is not None},{sw is not None})")
     Xd = upload_padded(X, in_dtype, pad)
     Wd = upload_padded(W, in_dtype, pad)
-    bd = dev(b, in_dtype) if bias else None
+    bd = dev(b, vec_dt) if bias else None
     n_out = N // 2 if act == "swiglu" else N
     ops, keep = [], {}
     if residual:
@@ -89,6 +100,13 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
     if split:
         keep["split"] = [Guarded(M, N // split, out_dtype) for _ in range(split)]
         ops.append(B.op(B.OP_SPLIT_COLS, split=[s.view for s in keep["split"]]))
+    if sa is not None:
+        keep["sa"] = dev(sa, I.F32)
+        ops.append(B.op(B.OP_DEQUANT_ROW, keep["sa"]))
+    if sw is not None:
+        keep["sw"] = dev(sw, I.F32)
+        ops.append(B.op(B.OP_DEQUANT_COL, keep["sw"]))
+    if split:
         y = None
     elif inplace:
         y = keep["z"]
@@ -99,8 +117,11 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
     assert st == B.OK, B.status_string(st)
     torch.cuda.synchronize()
 
-    ref = O.linear_epilogue(I.to_f64(X, in_dtype), I.to_f64(W, in_dtype),
-                            bias=None if b is None else I.to_f64(b, in_dtype),
+    xv = O.e4m3_decode(X) if fp8 else I.to_f64(X, in_dtype)
+    wv = O.e4m3_decode(W) if fp8 else I.to_f64(W, in_dtype)
+    ref = O.linear_epilogue(xv, wv, bias=None if b is None else I.to_f64(b, vec_dt),
+                            x_scale=None if sa is None else sa.astype(np.float64),
+                            w_scale=None if sw is None else sw.astype(np.float64),
                             residual=None if z is None else I.to_f64(z, zdt),
                             col_scale=None if g is None else I.to_f64(g, zdt),
                             row_scale=None if r is None else r.astype(np.float64), act=act)
@@ -123,6 +144,14 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
         for i, sg in enumerate(keep["split"]):
             assert sg.intact()
             check_out(host64(sg.view), ref["y"][:, i * d:(i + 1) * d], out_dtype, f"split block {i}")
+    elif fp8 and out_dtype == I.F32:
+        mag = np.abs(xv) @ np.abs(wv).T
+        if sa is not None:
+            mag = mag * sa.astype(np.float64)[:, None]
+        if sw is not None:
+            mag = mag * sw.astype(np.float64)[None, :]
+        assert act != "swiglu"
+        check_f32_e4m3_acc(host64(y.view), ref["y"], 2.0 * mag, "Y")
     else:
         check_out(host64(y.view), ref["y"], out_dtype, "Y")
     if aux:
@@ -231,6 +260,52 @@ def test_swiglu_fp8_rows(M, N, K):
     check_fp8(host64(out["y"].view), s, y32, "codes vs own fp32 values")
     codes = host64(out["y"].view)
     assert all(((codes[m] & 0x7F) == 0x7E).any() for m in range(M) if s[m] > 0)
+
+
+# ---------------------------------------------------------------------------
+# E4M3 inputs, scale-after-accumulate: the 256 x 256 E4M3 kernel for every M; K = 160 and 272
+# end in a partial 128-code step, K = 16 is a single 16-code chunk.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 160), (17, 72, 64), (1, 8, 16), (520, 776, 272)])
+def test_fp8_input_bias_gelu(M, N, K):
+    run_linear(M, N, K, in_dtype=I.F8E4M3, bias=True, act="gelu_erf")
+
+
+def test_fp8_input_residual():
+    run_linear(300, 264, 160, in_dtype=I.F8E4M3, residual=True)
+
+
+def test_fp8_input_optional_scales_and_generic_chain():
+    run_linear(300, 264, 160, in_dtype=I.F8E4M3, dq_col=False, act="gelu_tanh", out_dtype=I.F32)
+    run_linear(300, 264, 160, in_dtype=I.F8E4M3, dq_row=False, dq_col=False, residual=True, aux=True,
+               partials=True, gamma=True, seed=1)
+    run_linear(70, 144, 48, in_dtype=I.F8E4M3, dq_row=False, bias=True, rscale=True, split=2, seed=2)
+
+
+def test_fp8_input_swiglu_fp8_output():
+    """E4M3 in, SwiGLU, E4M3 out. Near zero an output code step is finer than the E4M3 MFMA's
+    block-sum error, so (as for bf16 inputs, tier 2) the same kernel with an fp32 output gives
+    the pre-quantisation values: those are checked against the oracle under the accumulation
+    bound carried through SwiGLU to first order, the scales must be exactly fl32(max|y32| / 448)
+    and the codes within 1 ulp of y32 / s."""
+    M, N, K = 300, 528, 160
+    out = run_linear(M, N, K, in_dtype=I.F8E4M3, act="swiglu", quant=True, check=False)
+    y32 = host64(run_linear(M, N, K, in_dtype=I.F8E4M3, act="swiglu", out_dtype=I.F32, check=False)["y"].view)
+    sa = host64(out["keep"]["sa"])
+    sw = host64(out["keep"]["sw"])
+    mag = (np.abs(O.e4m3_decode(out["X"])) @ np.abs(O.e4m3_decode(out["W"])).T) * sa[:, None] * sw[None, :]
+    h = out["ref"]["h1"]
+    g, u = h[:, 0::2], h[:, 1::2]
+    # |d silu(g) u| <= 1.1 |u| |dg| + (|g| + 0.3) |du|  (|silu'| <= 1.1, |silu(g)| <= |g| + 0.3)
+    check_f32_e4m3_acc(y32, out["ref"]["y"], 1.1 * np.abs(u) * mag[:, 0::2] + (np.abs(g) + 0.3) * mag[:, 1::2],
+                       "pre-quantisation values")
+    s = host64(out["keep"]["s"].view[0]).astype(np.float32)
+    assert out["keep"]["s"].intact() and out["y"].intact()
+    assert np.array_equal(s, O.fp8_row_scale(np.abs(y32).max(axis=1).astype(np.float32))), \
+        "scale is not fl32(absmax / 448)"
+    check_fp8(host64(out["y"].view), s, y32, "codes vs own fp32 values")
+    assert workspace_ok(out["ws"])
 
 
 def test_fp8_rows_without_activation():
