@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix / vector
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "fused GEMM+epilogue TFLOP/s (%MFMA peak); LN+GELU GB/s (%HBM peak)"
 
@@ -48,6 +49,12 @@ SUITE = [
     ("linear_gelu_f32_64x256x256", "latency"),
 ]
 DOMINANT = "mlp_up_gelu_bf16_8192x16384x4096"
+# Widening beyond the suite above (E4M3 inputs): timed and reported under "next_workloads",
+# each against the fp8 MFMA peak, and not part of `value`.
+NEXT = [
+    ("downproj_residual_fp8in_16384x2048x8192", "mfma"),
+    ("mlp_up_gelu_fp8in_8192x16384x4096", "mfma"),
+]
 
 
 def time_workload(run, steps: int, warmup: int) -> float:
@@ -72,7 +79,7 @@ def copies_for(spec) -> int:
     if spec["kind"] == "ln":
         per = spec["rows"] * spec["cols"] * 2
     else:
-        es = 4 if spec["in_dtype"] == I.F32 else 2
+        es = {I.F32: 4, I.F8E4M3: 1}.get(spec["in_dtype"], 2)
         per = (spec["M"] + spec["N"]) * spec["K"] * es + (spec["M"] * spec["N"] * 2 if spec.get("residual") else 0)
     return max(1, min(8, -(-(300 << 20) // max(per, 1))))
 
@@ -174,8 +181,9 @@ def main() -> int:
     from gelu_bf16_gemm_amd import workloads as WL
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    names = [n for n, _ in SUITE] if args.only is None else args.only.split(",")
-    bound = dict(SUITE)
+    names = [n for n, _ in SUITE + NEXT] if args.only is None else args.only.split(",")
+    bound = dict(SUITE + NEXT)
+    suite = {n for n, _ in SUITE}
     results = {}
     calib = copy_calibration(args.steps) if args.copy_calibration else None
     for name in names:
@@ -191,7 +199,7 @@ def main() -> int:
         r = {"ms": round(ms, 5), "bound": bound.get(name, "mfma")}
         if fl:
             r["TFLOP/s"] = round(fl / ms / 1e9, 2)
-            peak = PEAK_F32_TFLOPS if spec.get("in_dtype") == I.F32 else PEAK_BF16_TFLOPS
+            peak = {I.F32: PEAK_F32_TFLOPS, I.F8E4M3: PEAK_FP8_TFLOPS}.get(spec.get("in_dtype"), PEAK_BF16_TFLOPS)
             r["mfma_frac"] = round(fl / ms / 1e9 / peak, 4)
         r["bytes"] = int(by)
         r["GB/s"] = round(by / ms / 1e6, 1)
@@ -201,11 +209,11 @@ def main() -> int:
         torch.cuda.empty_cache()
         print(f"[bench] {name}: {r}", file=sys.stderr, flush=True)
 
-    gemm = [n for n in names if I.WORKLOADS[n]["kind"] == "linear"]
+    gemm = [n for n in names if I.WORKLOADS[n]["kind"] == "linear" and n in suite]
     gemm_ms = sum(results[n]["ms"] for n in gemm)
     gemm_flops = sum(2.0 * I.WORKLOADS[n]["M"] * I.WORKLOADS[n]["N"] * I.WORKLOADS[n]["K"] for n in gemm)
     value = gemm_flops / gemm_ms / 1e9 if gemm_ms > 0 else 0.0
-    step_ms = sum(r["ms"] for r in results.values())
+    step_ms = sum(r["ms"] for n, r in results.items() if n in suite)
 
     roof = None
     if DOMINANT in results:
@@ -221,14 +229,15 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "fused-linear hot path suite (one pass of every workload at full size)",
-                   "workloads": names},
+                   "workloads": [n for n in names if n in suite]},
         "roofline": roof,
         "ln_gelu": None if ln is None else {
             "bound": "hbm", "achieved": ln["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ln["hbm_frac"],
             "traffic": measured_traffic("ln_gelu_fast_kernel", "ln_gelu_f16_32768x4096"),
             "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": int(ln["bytes"]),
             "kernel": "ln_gelu_fast_kernel", "workload": "ln_gelu_f16_32768x4096"},
-        "workloads": results,
+        "workloads": {n: r for n, r in results.items() if n in suite},
+        "next_workloads": {n: r for n, r in results.items() if n not in suite},
     }
     if calib is not None:
         line["copy_calibration"] = calib
