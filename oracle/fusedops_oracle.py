@@ -29,6 +29,9 @@ in the repository's design notes):
 * FP8 is OCP E4M3FN (max 448); s = fl32(absmax / 448); values are clamped to
   +-448 before round-to-nearest-even, so the encoder saturates, never NaN.
 * SwiGLU reads gate = column 2j and up = column 2j+1: y_j = silu(gate) * up.
+* RoPE: adjacent feature pairs (2i, 2i+1) rotate by the angle of pair index
+  (column mod d) / 2 of the row's token; cos / sin come from a per-row table
+  (the caller gathers it by position); with a Q/K/V split, V is not rotated.
 * FP8 inputs: one scale group spanning all of K, i.e. one activation scale per
   row of X and one weight scale per row of W (output channel); both multiply the
   fp32 accumulator before the bias, which stays a 16-bit float vector.
@@ -48,7 +51,7 @@ __all__ = [
     "layernorm_stats", "layernorm", "layernorm_gelu",
     "merge_sumsq", "merge_absmax", "merge_mean_m2", "merge_max_sumexp",
     "e4m3_values", "e4m3_decode", "e4m3_encode", "e4m3_ordinal",
-    "fp8_row_scale", "quantize_fp8_rows", "split_cols",
+    "fp8_row_scale", "quantize_fp8_rows", "split_cols", "rope_pairs", "rope_table",
 ]
 
 PARTIAL_COLS = 128          # public granularity of the RMSNorm row partials
@@ -189,6 +192,40 @@ def linear_epilogue(x, w, bias=None, residual=None, col_scale=None, row_scale=No
     else:
         raise ValueError(f"unknown activation {act!r}")
     return {"h1": h1, "partials": partials, "y": y}
+
+
+def rope_pairs(y: np.ndarray, cs: np.ndarray, d: int, rot_cols: int | None = None) -> np.ndarray:
+    """Rotate adjacent feature pairs: (a, b) -> (a cos - b sin, a sin + b cos).
+
+    [Epilogue] §背景 (RoPE rotates each adjacent pair of dimensions), §模式B (a pairwise map
+    returning two values), §末尾布局调整 (the width is unchanged) and §用形状与步长把约定钉死 (the
+    QKV output carries rotated Q and K segments, V as computed). Column pair
+    (2j, 2j+1) of row m uses the angle of pair index i = (2j mod d) / 2 within its head of d
+    columns: cos = cs[m, 2i], sin = cs[m, 2i+1]. Columns at or past rot_cols stay as they are.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    cs = np.asarray(cs, dtype=np.float64)
+    M, N = y.shape
+    rot = N if rot_cols is None else rot_cols
+    out = y.copy()
+    for c in range(0, rot, 2):
+        i = (c % d) // 2
+        cos, sin = cs[:, 2 * i], cs[:, 2 * i + 1]
+        a, b = y[:, c], y[:, c + 1]
+        out[:, c] = a * cos - b * sin
+        out[:, c + 1] = a * sin + b * cos
+    return out
+
+
+def rope_table(positions, d: int, base: float = 10000.0) -> np.ndarray:
+    """cos / sin of pos * base^(-2i/d) for i < d/2, interleaved per row (the usual RoPE
+    frequency schedule; used by pins only, the library takes any table)."""
+    pos = np.asarray(positions, dtype=np.float64)
+    inv = base ** (-2.0 * np.arange(d // 2) / d)
+    ang = pos[:, None] * inv[None, :]
+    cs = np.empty((pos.size, d))
+    cs[:, 0::2], cs[:, 1::2] = np.cos(ang), np.sin(ang)
+    return cs
 
 
 def split_cols(y: np.ndarray, n: int) -> list:

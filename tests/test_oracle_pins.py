@@ -179,6 +179,61 @@ def test_fp8_input_worked_example_bias_is_not_scaled():
     assert out["y"][0, 0] == pytest.approx(3.25 * 0.5 * (1.0 + math.erf(3.25 / math.sqrt(2.0))), rel=1e-15)
 
 
+# ---------------------------------------------------------------------------
+# RoPE pairwise epilogue
+# ---------------------------------------------------------------------------
+
+def test_rope_worked_examples():
+    # (1, 0) by 30 degrees -> (cos 30, sin 30); (a, b) by a quarter turn (cos 0, sin 1) -> (-b, a)
+    c30, s30 = math.sqrt(3.0) / 2.0, 0.5
+    out = O.rope_pairs(np.array([[1.0, 0.0, 3.0, -2.0]]), np.array([[c30, s30, 0.0, 1.0]]), d=4)
+    assert np.allclose(out, [[c30, s30, 2.0, 3.0]], rtol=0, atol=1e-15)
+    assert out[0, 2] == 2.0 and out[0, 3] == 3.0  # exact for the quarter turn
+
+
+def test_rope_inverse_norm_and_head_periodicity():
+    rng = np.random.default_rng(31)
+    M, d, heads = 5, 8, 3
+    y = rng.standard_normal((M, d * heads))
+    ang = rng.uniform(0, 2 * np.pi, size=(M, d // 2))
+    cs = np.empty((M, d))
+    cs[:, 0::2], cs[:, 1::2] = np.cos(ang), np.sin(ang)
+    inv = cs.copy()
+    inv[:, 1::2] *= -1.0
+    r = O.rope_pairs(y, cs, d)
+    np.testing.assert_allclose(O.rope_pairs(r, inv, d), y, rtol=0, atol=1e-12)   # rotate back
+    np.testing.assert_allclose(r[:, 0::2] ** 2 + r[:, 1::2] ** 2, y[:, 0::2] ** 2 + y[:, 1::2] ** 2,
+                               rtol=1e-12)                                          # pair norms kept
+    # every head of d columns uses the same d/2 angles
+    for h in range(heads):
+        np.testing.assert_allclose(r[:, h * d:(h + 1) * d], O.rope_pairs(y[:, h * d:(h + 1) * d], cs, d),
+                                   rtol=0, atol=0)
+
+
+def test_rope_leaves_unrotated_columns_and_v_block():
+    rng = np.random.default_rng(32)
+    y = rng.standard_normal((3, 12))
+    cs = O.rope_table([0, 5, 9], 4)
+    r = O.rope_pairs(y, cs, 4, rot_cols=8)  # Q, K of width 4 rotated, V (last 4) untouched
+    assert np.array_equal(r[:, 8:], y[:, 8:])
+    assert np.array_equal(O.rope_pairs(y, O.rope_table([0, 0, 0], 4), 4), y)  # position 0: identity
+
+
+def test_rope_scores_depend_on_position_difference_only():
+    # the defining property of rotary embeddings: q(p) . k(p') after rotation depends on p - p'
+    rng = np.random.default_rng(33)
+    d = 16
+    q = rng.standard_normal((1, d))
+    k = rng.standard_normal((1, d))
+    def score(p, pp):
+        qr = O.rope_pairs(q, O.rope_table([p], d), d)
+        kr = O.rope_pairs(k, O.rope_table([pp], d), d)
+        return float((qr * kr).sum())
+    assert score(7, 3) == pytest.approx(score(104, 100), rel=1e-9, abs=1e-9)
+    assert score(0, 0) == pytest.approx(float((q * k).sum()), rel=1e-12)
+    assert abs(score(7, 3) - score(7, 4)) > 1e-6
+
+
 def test_gelu_erf_textbook_normal_cdf():
     for x, phi in _load_cdf():
         assert O.gelu_erf(np.array([x]))[0] == pytest.approx(x * phi, rel=1e-15, abs=1e-16)
