@@ -33,7 +33,7 @@ lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 F32, BF16, F16, F8E4M3 = 0, 1, 2, 3
 (OP_RESIDUAL_ADD, OP_STORE_AUX, OP_ROWSUMSQ_PARTIAL, OP_COL_SCALE, OP_ROW_SCALE, OP_GELU_ERF,
- OP_GELU_TANH, OP_SWIGLU, OP_QUANT_FP8_ROW, OP_SPLIT_COLS, OP_DEQUANT_ROW, OP_DEQUANT_COL) = range(1, 13)
+ OP_GELU_TANH, OP_SWIGLU, OP_QUANT_FP8_ROW, OP_SPLIT_COLS, OP_DEQUANT_ROW, OP_DEQUANT_COL, OP_ROPE) = range(1, 14)
 GELU_NONE, GELU_TANH, GELU_ERF = 0, 1, 2
 PARTIAL_COLS = 128
 LN_MAX_COLS = 16384
@@ -114,9 +114,10 @@ def _stream(stream) -> int | None:
     return torch.cuda.current_stream().cuda_stream
 
 
-def op(kind: int, tensor=None, *, out=None, split=None) -> Op:
-    """Build one epilogue op. `tensor` is the op's input (z, gamma, r) and `out` its output
-    (h1, partials, scales); `split` is the list of SPLIT_COLS destination tensors."""
+def op(kind: int, tensor=None, *, out=None, split=None, head_dim=None) -> Op:
+    """Build one epilogue op. `tensor` is the op's input (z, gamma, r, scales, RoPE table) and
+    `out` its output (h1, partials, scales); `split` is the list of SPLIT_COLS destination
+    tensors; `head_dim` is ROPE's head width d."""
     o = Op()
     o.kind = kind
     t = tensor if tensor is not None else out
@@ -133,6 +134,8 @@ def op(kind: int, tensor=None, *, out=None, split=None) -> Op:
         o.dtype = dtype_code(split[0])
         for i, s in enumerate(split):
             o.out_v[i] = s.data_ptr()
+    if head_dim is not None:
+        o.n_split = head_dim
     return o
 
 

@@ -52,7 +52,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Parsed epilogue op list.
 struct OpList {
-  const fusedops_op* by_kind[13] = {};
+  const fusedops_op* by_kind[14] = {};
   int act = ACT_NONE;
   bool quant = false;
 };
@@ -63,7 +63,7 @@ int32_t parse_ops(const fusedops_op* ops, int32_t n_ops, OpList& out) {
   int n_act = 0;
   for (int i = 0; i < n_ops; ++i) {
     const fusedops_op& op = ops[i];
-    if (op.kind < FUSEDOPS_OP_RESIDUAL_ADD || op.kind > FUSEDOPS_OP_DEQUANT_COL) return FUSEDOPS_ERR_INVALID_ARG;
+    if (op.kind < FUSEDOPS_OP_RESIDUAL_ADD || op.kind > FUSEDOPS_OP_ROPE) return FUSEDOPS_ERR_INVALID_ARG;
     if (op.kind <= last) return FUSEDOPS_ERR_INVALID_ARG;  // increasing kind order, each kind once
     if (op.reserved != 0) return FUSEDOPS_ERR_INVALID_ARG;
     last = op.kind;
@@ -151,6 +151,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   const fusedops_op* op_split = ol.by_kind[FUSEDOPS_OP_SPLIT_COLS];
   const fusedops_op* op_dqr = ol.by_kind[FUSEDOPS_OP_DEQUANT_ROW];
   const fusedops_op* op_dqc = ol.by_kind[FUSEDOPS_OP_DEQUANT_COL];
+  const fusedops_op* op_rope = ol.by_kind[FUSEDOPS_OP_ROPE];
   const bool fp8_in = in_dtype == FUSEDOPS_F8E4M3;
   const bool swiglu = ol.act == ACT_SWIGLU;
   const int64_t n_out = swiglu ? N / 2 : N;
@@ -185,6 +186,13 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (op_q && !op_q->out) return FUSEDOPS_ERR_INVALID_ARG;
   if ((op_dqr || op_dqc) && !fp8_in) return FUSEDOPS_ERR_INVALID_ARG;  // scales of FP8 inputs only
   if ((op_dqr && !op_dqr->in) || (op_dqc && !op_dqc->in)) return FUSEDOPS_ERR_INVALID_ARG;
+  // RoPE: table of M rows, head width d a multiple of 8, rotated width a multiple of d
+  const int64_t rope_cols = op_rope ? (op_split ? N - N / op_split->n_split : N) : 0;
+  if (op_rope) {
+    if (!op_rope->in || op_rope->dtype != FUSEDOPS_F32 || swiglu) return FUSEDOPS_ERR_INVALID_ARG;
+    const int64_t d = op_rope->n_split;
+    if (d < 8 || d % 8 || op_rope->ld < d || rope_cols % d) return FUSEDOPS_ERR_INVALID_ARG;
+  }
   if (swiglu && (N % 2)) return FUSEDOPS_ERR_INVALID_ARG;
   if (ldx < K || ldw < K) return FUSEDOPS_ERR_INVALID_ARG;
   if (Y && ldy < n_out) return FUSEDOPS_ERR_INVALID_ARG;
@@ -203,6 +211,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (op_row && !aligned(op_row->in, 4)) return FUSEDOPS_ERR_MISALIGNED;
   if (op_q && !aligned(op_q->out, 4)) return FUSEDOPS_ERR_MISALIGNED;
   if ((op_dqr && !aligned(op_dqr->in, 4)) || (op_dqc && !aligned(op_dqc->in, 4))) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_rope && (!aligned(op_rope->in, 16) || op_rope->ld % 4)) return FUSEDOPS_ERR_MISALIGNED;
   if (op_split) {
     if ((N / op_split->n_split) % 8) return FUSEDOPS_ERR_MISALIGNED;
     if ((op_split->ld * es_out) % 16) return FUSEDOPS_ERR_MISALIGNED;
@@ -211,14 +220,15 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   }
 
   // ---- aliasing: outputs may not overlap inputs or each other, except Y == z exactly
-  constexpr int kInSpans = 8;
+  constexpr int kInSpans = 9;
   Span in_spans[kInSpans] = {
       span2d(X, M, K, ldx, es_in), span2d(W, N, K, ldw, es_in), span2d(bias, 1, N, N, dtype_size(bias_dtype)),
       op_res ? span2d(op_res->in, M, N, op_res->ld, dtype_size(op_res->dtype)) : Span{},
       op_gam ? span2d(op_gam->in, 1, N, N, dtype_size(op_gam->dtype)) : Span{},
       op_row ? span2d(op_row->in, 1, M, M, 4) : Span{},
       op_dqr ? span2d(op_dqr->in, 1, M, M, 4) : Span{},
-      op_dqc ? span2d(op_dqc->in, 1, N, N, 4) : Span{}};
+      op_dqc ? span2d(op_dqc->in, 1, N, N, 4) : Span{},
+      op_rope ? span2d(op_rope->in, M, op_rope->n_split, op_rope->ld, 4) : Span{}};
   Span out_spans[6];
   int n_out_spans = 0;
   if (Y) out_spans[n_out_spans++] = span2d(Y, M, n_out, ldy, es_out);
@@ -281,6 +291,12 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   e.bias = bias; e.bias_dtype = bias_dtype;
   if (op_dqr) e.dq_row = static_cast<const float*>(op_dqr->in);
   if (op_dqc) e.dq_col = static_cast<const float*>(op_dqc->in);
+  if (op_rope) {
+    e.rope_cs = static_cast<const float*>(op_rope->in);
+    e.rope_ld = op_rope->ld;
+    e.rope_d = (int)op_rope->n_split;
+    e.rope_cols = (int)rope_cols;
+  }
   if (op_res) { e.z = op_res->in; e.ldz = op_res->ld; e.z_dtype = op_res->dtype; }
   if (op_aux) { e.aux = op_aux->out; e.ld_aux = op_aux->ld; e.aux_dtype = op_aux->dtype; }
   if (op_par) { e.partials = static_cast<float*>(op_par->out); e.ldp = op_par->ld; }

@@ -34,6 +34,10 @@ struct EpiParams {
   const float* rscale;
   const float* dq_row;    // FP8 inputs: activation scale per row of X (null: 1)
   const float* dq_col;    // FP8 inputs: weight scale per output channel (null: 1)
+  const float* rope_cs;   // RoPE: per-row cos / sin table (null: no rotation)
+  int64_t rope_ld;        //   its row stride in floats
+  int rope_d;             //   head width (pair index i = (column mod d) / 2)
+  int rope_cols;          //   columns [0, rope_cols) rotated
   int act;
   int quant;              // FP8 per-row quantised writeback
   float* scales;
@@ -335,6 +339,19 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
       for (int j = 0; j < 4; ++j) v[j] = silu_f32(v[2 * j]) * v[2 * j + 1];
 #pragma unroll
       for (int j = 4; j < 8; ++j) v[j] = 0.f;
+    }
+    // RoPE on adjacent pairs: the thread's 8 columns lie in one head (d is a multiple of 8)
+    if (e.rope_cs && ok && f < e.rope_cols) {
+      const float* cs = e.rope_cs + (int64_t)t * e.rope_ld + (f % e.rope_d);
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
+      const float cv[4] = {c0[0], c0[2], c1[0], c1[2]}, sv[4] = {c0[1], c0[3], c1[1], c1[3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = v[2 * j], x1 = v[2 * j + 1];
+        v[2 * j] = x0 * cv[j] - x1 * sv[j];
+        v[2 * j + 1] = x0 * sv[j] + x1 * cv[j];
+      }
     }
     const int fo = swiglu ? f / 2 : f;  // output column of v[0]
 

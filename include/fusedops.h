@@ -62,7 +62,7 @@ enum fusedops_dtype {
  * Epilogue op kinds. An op list is given in increasing kind value, each kind at
  * most once, and with at most one of GELU_ERF / GELU_TANH / SWIGLU. With
  * acc = X W^T the chain is, per output element (m, n) (the two DEQUANT kinds,
- * listed last, act first):
+ * numbered after the others, act first):
  *
  *   acc = acc * sa[m] * sw[n]           DEQUANT_ROW (sa), DEQUANT_COL (sw); FP8 inputs only
  *                                       [Epilogue] §量化尾声的完整形态 (per-group scales, one group)
@@ -73,6 +73,7 @@ enum fusedops_dtype {
  *   h2 = h1 * gamma[n]                  COL_SCALE                   [Epilogue] §模式A, Epilogue 1
  *   h3 = r[m] * h2                      ROW_SCALE                   [Epilogue] §模式A, Epilogue 2
  *   y  = act(h3)                        GELU_ERF | GELU_TANH | SWIGLU
+ *   y  = rotate(y)                      ROPE: adjacent column pairs   [Epilogue] §背景, §模式B
  *   QUANT_FP8_ROW: Y is E4M3 codes with one fp32 scale per row    [Epilogue] §仿射量化与尾声的五步
  *   SPLIT_COLS: Y is written as n_split column blocks              [Fusion] §QKV投影融合
  *
@@ -101,6 +102,13 @@ enum fusedops_dtype {
  *                     F8E4M3. Absent: sa = 1.
  *   DEQUANT_COL       in = sw (fp32, length N): the weight scale of each output channel (row of W).
  *                     Requires in_dtype = F8E4M3. Absent: sw = 1.
+ *   ROPE              in = table (fp32, M rows, row stride ld >= d floats), n_split = d (head width,
+ *                     a multiple of 8). Column pair (2j, 2j+1) of output row m, with i = (2j mod d)/2,
+ *                     becomes (a c - b s, a s + b c) where c = table[m][2i], s = table[m][2i+1]: row
+ *                     m holds the cos / sin of its token's rotation angles, so the caller gathers
+ *                     the table by position. Rotated: every column, or with SPLIT_COLS every block
+ *                     but the last (Q and K rotated, V not: [Epilogue] §用形状与步长把约定钉死); the
+ *                     rotated width must be a multiple of d. Not combinable with SWIGLU.
  */
 enum fusedops_op_kind {
   FUSEDOPS_OP_RESIDUAL_ADD = 1,
@@ -114,7 +122,8 @@ enum fusedops_op_kind {
   FUSEDOPS_OP_QUANT_FP8_ROW = 9,
   FUSEDOPS_OP_SPLIT_COLS = 10,
   FUSEDOPS_OP_DEQUANT_ROW = 11,
-  FUSEDOPS_OP_DEQUANT_COL = 12
+  FUSEDOPS_OP_DEQUANT_COL = 12,
+  FUSEDOPS_OP_ROPE = 13
 };
 
 enum fusedops_gelu_form {

@@ -98,6 +98,26 @@ def test_fp8_input_rules():
     assert lin(in_dt=B.F8E4M3, ops=[mkop(B.OP_DEQUANT_ROW, dtype=B.F32, inp=addr(5) + 2)]) == B.ERR_MISALIGNED
 
 
+def test_rope_rules():
+    # every case is refused before any launch (the addresses are placeholders); N = 64
+    def rope(d, ld=64, inp=addr(7), dtype=B.F32):
+        o = mkop(B.OP_ROPE, dtype=dtype, inp=inp, ld=ld)
+        o.n_split = d
+        return o
+    assert lin(ops=[rope(12)]) == B.ERR_INVALID_ARG                     # d not a multiple of 8
+    assert lin(ops=[rope(0)]) == B.ERR_INVALID_ARG
+    assert lin(ops=[rope(48)]) == B.ERR_INVALID_ARG                     # 64 columns not a multiple of d
+    assert lin(ops=[rope(32, ld=16)]) == B.ERR_INVALID_ARG              # ld < d
+    assert lin(ops=[rope(32, inp=None)]) == B.ERR_INVALID_ARG           # no table
+    assert lin(ops=[rope(32, dtype=B.BF16)]) == B.ERR_INVALID_ARG       # table must be fp32
+    assert lin(N=64, ldy=32, ops=[mkop(B.OP_SWIGLU), rope(32)]) == B.ERR_INVALID_ARG  # not with SwiGLU
+    assert lin(ops=[rope(32, ld=34)]) == B.ERR_MISALIGNED               # 136-byte table rows
+    assert lin(ops=[rope(32, inp=addr(7, 8))]) == B.ERR_MISALIGNED
+    assert lin(ops=[rope(32, inp=addr(2))]) == B.ERR_INVALID_ARG        # table overlaps Y
+    split = mkop(B.OP_SPLIT_COLS, out_v=[addr(3), addr(4), addr(5)], n_split=3, ld=32)
+    assert lin(N=96, Y=None, ops=[split, rope(48)]) == B.ERR_INVALID_ARG  # Q+K width 64 vs d = 48
+
+
 def test_op_list_rules():
     gelu, tanh, sw = mkop(B.OP_GELU_ERF), mkop(B.OP_GELU_TANH), mkop(B.OP_SWIGLU)
     res = mkop(B.OP_RESIDUAL_ADD, inp=addr(5), ld=64)

@@ -39,7 +39,7 @@ def upload_padded(stored, dtype, pad):
 
 def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=None, residual=False,
                aux=False, partials=False, gamma=False, rscale=False, split=0, quant=False, seed=0,
-               pad=0, inplace=False, aux_dtype=None, z_dtype=None, dq_row=True, dq_col=True, check=True):
+               pad=0, inplace=False, aux_dtype=None, z_dtype=None, dq_row=True, dq_col=True, rope=0, check=True):
     rng = np.random.default_rng([101, M, N, K, seed])
     fp8 = in_dtype == I.F8E4M3
     sa = sw = None
@@ -58,10 +58,16 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
     z = I.random_stored(rng, (M, N), zdt) if residual else None
     g = I.random_stored(rng, (N,), zdt, mean=1.0, std=0.1) if gamma else None
     r = rng.uniform(0.5, 1.5, M).astype(np.float32) if rscale else None
+    cs = None
+    if rope:
+        # per-row RoPE table: cos / sin of random angles for the rope / 2 pair indices
+        ang = rng.uniform(0.0, 2.0 * math.pi, size=(M, rope // 2))
+        cs = np.empty((M, rope), np.float32)
+        cs[:, 0::2], cs[:, 1::2] = np.cos(ang), np.sin(ang)
 
     note(f"linear M={M} N={N} K={K} in={in_dtype} out={out_dtype} act={act} bias={bias} res={residual} "
          f"aux={aux} partials={partials} gamma={gamma} rscale={rscale} split={split} quant={quant} "
-         f"pad={pad} inplace={inplace} seed={seed} dq=({sa is not None},{sw is not None})")
+         f"pad={pad} inplace={inplace} seed={seed} dq=({sa is not None},{sw is not None}) rope={rope}")
     Xd = upload_padded(X, in_dtype, pad)
     Wd = upload_padded(W, in_dtype, pad)
     bd = dev(b, vec_dt) if bias else None
@@ -106,6 +112,9 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
     if sw is not None:
         keep["sw"] = dev(sw, I.F32)
         ops.append(B.op(B.OP_DEQUANT_COL, keep["sw"]))
+    if cs is not None:
+        keep["cs"] = dev(cs, I.F32)
+        ops.append(B.op(B.OP_ROPE, keep["cs"], head_dim=rope))
     if split:
         y = None
     elif inplace:
@@ -125,6 +134,8 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
                             residual=None if z is None else I.to_f64(z, zdt),
                             col_scale=None if g is None else I.to_f64(g, zdt),
                             row_scale=None if r is None else r.astype(np.float64), act=act)
+    if cs is not None:
+        ref["y"] = O.rope_pairs(ref["y"], cs.astype(np.float64), rope, N - N // split if split else N)
     out = {"ref": ref, "keep": keep, "y": y, "ws": ws, "X": X, "W": W}
     if not check:
         return out
@@ -306,6 +317,25 @@ def test_fp8_input_swiglu_fp8_output():
         "scale is not fl32(absmax / 448)"
     check_fp8(host64(out["y"].view), s, y32, "codes vs own fp32 values")
     assert workspace_ok(out["ws"])
+
+
+# ---------------------------------------------------------------------------
+# RoPE on adjacent pairs (per-row cos / sin table); with a Q/K/V split, V is left as computed
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(300, 384, 136), (17, 192, 40), (520, 768, 264)])
+def test_rope_qkv_split(M, N, K):
+    run_linear(M, N, K, bias=True, split=3, rope=64)
+
+
+def test_rope_full_width_after_activation():
+    run_linear(129, 512, 64, act="gelu_tanh", rope=128)
+    run_linear(300, 264, 136, bias=True, rope=8, out_dtype=I.F32, seed=1)
+
+
+def test_rope_fp8_inputs_and_fp8_output():
+    run_linear(300, 384, 160, in_dtype=I.F8E4M3, bias=True, split=3, rope=64)
+    run_linear(70, 256, 72, rope=32, quant=True)
 
 
 def test_fp8_rows_without_activation():
