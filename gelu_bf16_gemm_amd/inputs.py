@@ -113,6 +113,10 @@ WORKLOADS = {
     "prefill_swiglu_fp8_bf16_16384x16384x2048": dict(config_id=9, kind="linear", M=16384, N=16384,
                                                      K=2048, in_dtype=BF16, bias=False, act="swiglu",
                                                      quant_fp8=True, out_dtype=F8E4M3),
+    # The fused QKV projection with RoPE on its Q and K blocks (head width 128).
+    "qkv_bias_rope_split_bf16_4096x12288x4096": dict(config_id=12, kind="linear", M=4096, N=12288,
+                                                     K=4096, in_dtype=BF16, bias=True, act=None,
+                                                     split=3, rope=128, out_dtype=BF16),
     # E4M3 inputs with per-row activation and per-channel weight scales: the down-projection
     # that consumes the quantised SwiGLU output above, with its residual add.
     "downproj_residual_fp8in_16384x2048x8192": dict(config_id=10, kind="linear", M=16384, N=2048,
@@ -125,7 +129,7 @@ WORKLOADS = {
 }
 
 # tensor ids inside one config
-_T_X, _T_W, _T_B, _T_Z, _T_GAMMA, _T_BETA, _T_SA, _T_SW = 0, 1, 2, 3, 4, 5, 6, 7
+_T_X, _T_W, _T_B, _T_Z, _T_GAMMA, _T_BETA, _T_SA, _T_SW, _T_ROPE = 0, 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def random_e4m3_codes(rng: np.random.Generator, shape, e_lo: int = 4, e_hi: int = 10) -> np.ndarray:
@@ -167,6 +171,13 @@ def make_linear_inputs(spec: dict, seed: int = 0, M: int | None = None, N: int |
         out["z"] = store(normal(rng_for(cid, _T_Z, seed), (M, N)), vec_dt)
     if spec.get("col_scale"):
         out["gamma"] = store(normal(rng_for(cid, _T_GAMMA, seed), (N,), mean=1.0, std=0.1), vec_dt)
+    if spec.get("rope"):
+        # per-row cos / sin of uniformly drawn angles (a rotation table; no frequency schedule)
+        d = spec["rope"]
+        ang = rng_for(cid, _T_ROPE, seed).uniform(0.0, 2.0 * np.pi, size=(M, d // 2))
+        cs = np.empty((M, d), np.float32)
+        cs[:, 0::2], cs[:, 1::2] = np.cos(ang), np.sin(ang)
+        out["rope_cs"] = cs
     return out
 
 

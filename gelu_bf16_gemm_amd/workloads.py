@@ -46,6 +46,7 @@ class LinearRun:
         self.b = to_device(inp["b"], vec_dt) if "b" in inp else None
         self.sa = to_device(inp["sa"], I.F32) if "sa" in inp else None
         self.sw = to_device(inp["sw"], I.F32) if "sw" in inp else None
+        self.rope_cs = to_device(inp["rope_cs"], I.F32) if "rope_cs" in inp else None
         self.z = [to_device(inp["z"], I.BF16) for _ in range(copies)] if "z" in inp else None
         self.gamma = to_device(inp["gamma"], I.BF16) if "gamma" in inp else None
         act = spec.get("act")
@@ -98,6 +99,8 @@ class LinearRun:
             ops.append(B.op(B.OP_DEQUANT_ROW, self.sa))
         if self.sw is not None:
             ops.append(B.op(B.OP_DEQUANT_COL, self.sw))
+        if self.rope_cs is not None:
+            ops.append(B.op(B.OP_ROPE, self.rope_cs, head_dim=s["rope"]))
         return ops
 
     def launch(self, i: int = 0, stream=None) -> None:
@@ -147,6 +150,8 @@ class LinearRun:
             b += M * 4
         if self.sw is not None:
             b += N * 4
+        if self.rope_cs is not None:
+            b += self.rope_cs.numel() * 4
         if self.z is not None:
             b += M * N * 2
         if self.aux is not None:

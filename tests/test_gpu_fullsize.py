@@ -48,6 +48,10 @@ def test_linear_workload_full_size(name):
                             act=spec.get("act"),
                             x_scale=inp["sa"][rows].astype(np.float64) if "sa" in inp else None,
                             w_scale=inp["sw"].astype(np.float64) if "sw" in inp else None)
+    if "rope_cs" in inp:
+        N, d = spec["N"], spec["rope"]
+        ref["y"] = O.rope_pairs(ref["y"], inp["rope_cs"][rows].astype(np.float64), d,
+                                N - N // spec["split"] if spec.get("split") else N)
     out = run.outputs(rows)
     if spec.get("quant_fp8"):
         s = out["scales"].astype(np.float32)
