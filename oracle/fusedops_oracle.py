@@ -51,7 +51,7 @@ __all__ = [
     "layernorm_stats", "layernorm", "layernorm_gelu",
     "merge_sumsq", "merge_absmax", "merge_mean_m2", "merge_max_sumexp",
     "e4m3_values", "e4m3_decode", "e4m3_encode", "e4m3_ordinal",
-    "fp8_row_scale", "quantize_fp8_rows", "split_cols", "rope_pairs", "rope_table",
+    "fp8_row_scale", "quantize_fp8_rows", "split_cols", "rope_pairs", "rope_table", "pattern_a_chain",
 ]
 
 PARTIAL_COLS = 128          # public granularity of the RMSNorm row partials
@@ -259,6 +259,24 @@ def rmsnorm_apply(r: np.ndarray, h: np.ndarray, gamma=None) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # LayerNorm + GELU rows
 # ---------------------------------------------------------------------------
+
+def pattern_a_chain(x, w0, z, gamma, w1, eps: float, act=None, h2_stored=None) -> dict:
+    """GEMM -> residual -> RMSNorm -> GEMM with the row scale deferred ([Epilogue] §模式A):
+
+        Epilogue 1: h1 = x W0 + z,  h2 = h1 * gamma,  partials of h1 (128-column chunks)
+        r = 1 / sqrt(sum_t p[m,t] / N1 + eps)           (the light aux reduction)
+        Epilogue 2: y = act(r[m] * (h2 W1))
+
+    `h2_stored`, when given, is the stored (rounded) h2 the second GEMM actually reads;
+    otherwise the exact h2 is used. Returns h1, h2, partials, r and y.
+    """
+    e1 = linear_epilogue(x, w0, residual=z, col_scale=gamma)
+    h1, h2 = e1["h1"], e1["y"]
+    r = rmsnorm_finalize(e1["partials"], h1.shape[1], eps)
+    x2 = h2 if h2_stored is None else np.asarray(h2_stored, dtype=np.float64)
+    e2 = linear_epilogue(x2, w1, row_scale=r, act=act)
+    return {"h1": h1, "h2": h2, "partials": e1["partials"], "r": r, "y": e2["y"]}
+
 
 def layernorm_stats(x: np.ndarray):
     """Per-row mean and biased variance, two passes: mu = sum x / N, var = sum (x-mu)^2 / N.

@@ -234,6 +234,28 @@ def test_rope_scores_depend_on_position_difference_only():
     assert abs(score(7, 3) - score(7, 4)) > 1e-6
 
 
+# ---------------------------------------------------------------------------
+# pattern A: the deferred row scale
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", [None, "swiglu"])
+def test_pattern_a_equals_normalising_before_the_second_gemm(act):
+    # (r h1 gamma) W1 = r (h1 gamma) W1 row by row: the deferred form equals RMSNorm first
+    rng = np.random.default_rng(41)
+    M, K0, N1, N2 = 6, 9, 260, 10
+    x, w0 = rng.standard_normal((M, K0)), rng.standard_normal((N1, K0))
+    z, gamma = rng.standard_normal((M, N1)), 1.0 + 0.1 * rng.standard_normal(N1)
+    w1 = rng.standard_normal((N2, N1))
+    out = O.pattern_a_chain(x, w0, z, gamma, w1, 1e-6, act=act)
+    h1 = x @ w0.T + z
+    normed = h1 / np.sqrt((h1 * h1).mean(axis=1, keepdims=True) + 1e-6) * gamma[None, :]
+    direct = normed @ w1.T
+    if act == "swiglu":
+        direct = direct[:, 0::2] / (1.0 + np.exp(-direct[:, 0::2])) * direct[:, 1::2]
+    np.testing.assert_allclose(out["y"], direct, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(out["r"], 1.0 / np.sqrt((h1 * h1).mean(axis=1) + 1e-6), rtol=1e-12)
+
+
 def test_gelu_erf_textbook_normal_cdf():
     for x, phi in _load_cdf():
         assert O.gelu_erf(np.array([x]))[0] == pytest.approx(x * phi, rel=1e-15, abs=1e-16)
