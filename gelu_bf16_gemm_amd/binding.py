@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import struct
 
 # torch brings its own HIP runtime (libamdhip64.so.7). Import it before loading the library so
 # that the library's libamdhip64.so.7 dependency resolves to that already-loaded runtime: one
@@ -33,7 +34,8 @@ lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 F32, BF16, F16, F8E4M3 = 0, 1, 2, 3
 (OP_RESIDUAL_ADD, OP_STORE_AUX, OP_ROWSUMSQ_PARTIAL, OP_COL_SCALE, OP_ROW_SCALE, OP_GELU_ERF,
- OP_GELU_TANH, OP_SWIGLU, OP_QUANT_FP8_ROW, OP_SPLIT_COLS, OP_DEQUANT_ROW, OP_DEQUANT_COL, OP_ROPE) = range(1, 14)
+ OP_GELU_TANH, OP_SWIGLU, OP_QUANT_FP8_ROW, OP_SPLIT_COLS, OP_DEQUANT_ROW, OP_DEQUANT_COL, OP_ROPE,
+ OP_ROW_RMS) = range(1, 15)
 GELU_NONE, GELU_TANH, GELU_ERF = 0, 1, 2
 PARTIAL_COLS = 128
 LN_MAX_COLS = 16384
@@ -136,6 +138,14 @@ def op(kind: int, tensor=None, *, out=None, split=None, head_dim=None) -> Op:
             o.out_v[i] = s.data_ptr()
     if head_dim is not None:
         o.n_split = head_dim
+    return o
+
+
+def row_rms_op(partials, width: int, eps: float) -> Op:
+    """ROW_RMS: the deferred RMSNorm row scale from a previous call's row partials."""
+    o = op(OP_ROW_RMS, partials)
+    o.n_split = width
+    o.reserved = int.from_bytes(struct.pack("<f", eps), "little", signed=True)
     return o
 
 

@@ -54,7 +54,7 @@ __host__ __device__ inline uint32_t config_of(const EpiParams& e) {
   if (e.aux) ops |= kAux;
   if (e.partials) ops |= kPart;
   if (e.gamma) ops |= kGamma;
-  if (e.rscale) ops |= kRscale;
+  if (e.rscale || e.rms_p) ops |= kRscale;
   if (e.quant) ops |= kQuant;
   if (e.n_split) ops |= kSplit;
   if (e.rope_cs) ops |= kRope;
@@ -71,7 +71,7 @@ struct Cfg {
   __device__ bool aux() const { if constexpr (S) return F & kAux; else return e.aux != nullptr; }
   __device__ bool part() const { if constexpr (S) return F & kPart; else return e.partials != nullptr; }
   __device__ bool gamma() const { if constexpr (S) return F & kGamma; else return e.gamma != nullptr; }
-  __device__ bool rscale() const { if constexpr (S) return F & kRscale; else return e.rscale != nullptr; }
+  __device__ bool rscale() const { if constexpr (S) return F & kRscale; else return e.rscale || e.rms_p; }
   __device__ bool quant() const { if constexpr (S) return F & kQuant; else return e.quant != 0; }
   __device__ bool split() const { if constexpr (S) return F & kSplit; else return e.n_split != 0; }
   __device__ int act() const { if constexpr (S) return (F >> kActShift) & 3; else return e.act; }
@@ -154,7 +154,7 @@ struct VecPrefetch {
     const int f = f0 + tid, t = t0 + tid;
     v[0] = cfg.bias() && f < N ? load1(e.bias, cfg.bias_dt(), f) : 0.f;
     v[1] = cfg.gamma() && f < N ? load1(e.gamma, cfg.gamma_dt(), f) : 1.f;
-    v[2] = cfg.rscale() && t < M ? e.rscale[t] : 0.f;
+    v[2] = cfg.rscale() && t < M ? row_scale_of(e, t) : 0.f;
   }
   __device__ __forceinline__ void store(float* svec) const {
     const int tid = threadIdx.x;

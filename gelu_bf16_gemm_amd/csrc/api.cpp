@@ -52,7 +52,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Parsed epilogue op list.
 struct OpList {
-  const fusedops_op* by_kind[14] = {};
+  const fusedops_op* by_kind[15] = {};
   int act = ACT_NONE;
   bool quant = false;
 };
@@ -63,9 +63,9 @@ int32_t parse_ops(const fusedops_op* ops, int32_t n_ops, OpList& out) {
   int n_act = 0;
   for (int i = 0; i < n_ops; ++i) {
     const fusedops_op& op = ops[i];
-    if (op.kind < FUSEDOPS_OP_RESIDUAL_ADD || op.kind > FUSEDOPS_OP_ROPE) return FUSEDOPS_ERR_INVALID_ARG;
+    if (op.kind < FUSEDOPS_OP_RESIDUAL_ADD || op.kind > FUSEDOPS_OP_ROW_RMS) return FUSEDOPS_ERR_INVALID_ARG;
     if (op.kind <= last) return FUSEDOPS_ERR_INVALID_ARG;  // increasing kind order, each kind once
-    if (op.reserved != 0) return FUSEDOPS_ERR_INVALID_ARG;
+    if (op.reserved != 0 && op.kind != FUSEDOPS_OP_ROW_RMS) return FUSEDOPS_ERR_INVALID_ARG;
     last = op.kind;
     out.by_kind[op.kind] = &op;
     if (op.kind == FUSEDOPS_OP_GELU_ERF || op.kind == FUSEDOPS_OP_GELU_TANH || op.kind == FUSEDOPS_OP_SWIGLU)
@@ -152,6 +152,10 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   const fusedops_op* op_dqr = ol.by_kind[FUSEDOPS_OP_DEQUANT_ROW];
   const fusedops_op* op_dqc = ol.by_kind[FUSEDOPS_OP_DEQUANT_COL];
   const fusedops_op* op_rope = ol.by_kind[FUSEDOPS_OP_ROPE];
+  const fusedops_op* op_rms = ol.by_kind[FUSEDOPS_OP_ROW_RMS];
+  float rms_eps = 0.f;
+  if (op_rms) std::memcpy(&rms_eps, &op_rms->reserved, sizeof(float));
+  const int64_t rms_T = op_rms ? cdiv(op_rms->n_split, FUSEDOPS_PARTIAL_COLS) : 0;
   const bool fp8_in = in_dtype == FUSEDOPS_F8E4M3;
   const bool swiglu = ol.act == ACT_SWIGLU;
   const int64_t n_out = swiglu ? N / 2 : N;
@@ -186,6 +190,10 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (op_q && !op_q->out) return FUSEDOPS_ERR_INVALID_ARG;
   if ((op_dqr || op_dqc) && !fp8_in) return FUSEDOPS_ERR_INVALID_ARG;  // scales of FP8 inputs only
   if ((op_dqr && !op_dqr->in) || (op_dqc && !op_dqc->in)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (op_rms) {
+    if (op_row || !op_rms->in || op_rms->n_split < 1 || op_rms->ld < rms_T) return FUSEDOPS_ERR_INVALID_ARG;
+    if (!(rms_eps > 0.f) || !std::isfinite(rms_eps)) return FUSEDOPS_ERR_INVALID_ARG;
+  }
   // RoPE: table of M rows, head width d a multiple of 8, rotated width a multiple of d
   const int64_t rope_cols = op_rope ? (op_split ? N - N / op_split->n_split : N) : 0;
   if (op_rope) {
@@ -212,6 +220,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (op_q && !aligned(op_q->out, 4)) return FUSEDOPS_ERR_MISALIGNED;
   if ((op_dqr && !aligned(op_dqr->in, 4)) || (op_dqc && !aligned(op_dqc->in, 4))) return FUSEDOPS_ERR_MISALIGNED;
   if (op_rope && (!aligned(op_rope->in, 16) || op_rope->ld % 4)) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_rms && !aligned(op_rms->in, 4)) return FUSEDOPS_ERR_MISALIGNED;
   if (op_split) {
     if ((N / op_split->n_split) % 8) return FUSEDOPS_ERR_MISALIGNED;
     if ((op_split->ld * es_out) % 16) return FUSEDOPS_ERR_MISALIGNED;
@@ -220,7 +229,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   }
 
   // ---- aliasing: outputs may not overlap inputs or each other, except Y == z exactly
-  constexpr int kInSpans = 9;
+  constexpr int kInSpans = 10;
   Span in_spans[kInSpans] = {
       span2d(X, M, K, ldx, es_in), span2d(W, N, K, ldw, es_in), span2d(bias, 1, N, N, dtype_size(bias_dtype)),
       op_res ? span2d(op_res->in, M, N, op_res->ld, dtype_size(op_res->dtype)) : Span{},
@@ -228,7 +237,8 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
       op_row ? span2d(op_row->in, 1, M, M, 4) : Span{},
       op_dqr ? span2d(op_dqr->in, 1, M, M, 4) : Span{},
       op_dqc ? span2d(op_dqc->in, 1, N, N, 4) : Span{},
-      op_rope ? span2d(op_rope->in, M, op_rope->n_split, op_rope->ld, 4) : Span{}};
+      op_rope ? span2d(op_rope->in, M, op_rope->n_split, op_rope->ld, 4) : Span{},
+      op_rms ? span2d(op_rms->in, M, rms_T, op_rms->ld, 4) : Span{}};
   Span out_spans[6];
   int n_out_spans = 0;
   if (Y) out_spans[n_out_spans++] = span2d(Y, M, n_out, ldy, es_out);
@@ -291,6 +301,13 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   e.bias = bias; e.bias_dtype = bias_dtype;
   if (op_dqr) e.dq_row = static_cast<const float*>(op_dqr->in);
   if (op_dqc) e.dq_col = static_cast<const float*>(op_dqc->in);
+  if (op_rms) {
+    e.rms_p = static_cast<const float*>(op_rms->in);
+    e.rms_ldp = op_rms->ld;
+    e.rms_T = (int)rms_T;
+    e.rms_n = (int)op_rms->n_split;
+    e.rms_eps = rms_eps;
+  }
   if (op_rope) {
     e.rope_cs = static_cast<const float*>(op_rope->in);
     e.rope_ld = op_rope->ld;

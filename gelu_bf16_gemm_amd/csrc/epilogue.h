@@ -34,6 +34,11 @@ struct EpiParams {
   const float* rscale;
   const float* dq_row;    // FP8 inputs: activation scale per row of X (null: 1)
   const float* dq_col;    // FP8 inputs: weight scale per output channel (null: 1)
+  const float* rms_p;     // ROW_RMS: row partials of the previous layer (null: none)
+  int64_t rms_ldp;        //   their row stride
+  int rms_T;              //   partials per row
+  int rms_n;              //   width the partials cover
+  float rms_eps;
   const float* rope_cs;   // RoPE: per-row cos / sin table (null: no rotation)
   int64_t rope_ld;        //   its row stride in floats
   int rope_d;             //   head width (pair index i = (column mod d) / 2)
@@ -50,6 +55,16 @@ struct EpiParams {
   int n_split;            int64_t split_w; int64_t ldv;
   void* yv0;              void* yv1;       void* yv2;
 };
+
+// The row scale of token t: ROW_SCALE's r[t], or ROW_RMS's r computed from the token's row
+// partials with the formula of the finalize kernel, 1 / sqrt(sum / width + eps).
+__device__ inline float row_scale_of(const EpiParams& e, int t) {
+  if (e.rscale) return e.rscale[t];
+  const float* p = e.rms_p + (int64_t)t * e.rms_ldp;
+  float s = 0.f;
+  for (int i = 0; i < e.rms_T; ++i) s += p[i];
+  return 1.0f / sqrtf(s / (float)e.rms_n + e.rms_eps);
+}
 
 struct GemmArgs {
   const void* X; int64_t ldx;
@@ -322,8 +337,8 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     // column scale, row scale
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] *= gam[i];
-    if (e.rscale) {
-      const float rs = t_ok ? e.rscale[t] : 0.f;
+    if (e.rscale || e.rms_p) {
+      const float rs = t_ok ? row_scale_of(e, t) : 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] *= rs;
     }

@@ -71,7 +71,7 @@ enum fusedops_dtype {
  *        STORE_AUX writes h1            (rank-2 tile store)         [Epilogue] §六类尾声原语 item 4
  *        ROWSUMSQ_PARTIAL writes p[m,t] = sum_{n in chunk t} h1^2   [Epilogue] §模式A partialRMS
  *   h2 = h1 * gamma[n]                  COL_SCALE                   [Epilogue] §模式A, Epilogue 1
- *   h3 = r[m] * h2                      ROW_SCALE                   [Epilogue] §模式A, Epilogue 2
+ *   h3 = r[m] * h2                      ROW_SCALE, or ROW_RMS (r from row partials)  [Epilogue] §模式A, Epilogue 2
  *   y  = act(h3)                        GELU_ERF | GELU_TANH | SWIGLU
  *   y  = rotate(y)                      ROPE: adjacent column pairs   [Epilogue] §背景, §模式B
  *   QUANT_FP8_ROW: Y is E4M3 codes with one fp32 scale per row    [Epilogue] §仿射量化与尾声的五步
@@ -102,6 +102,13 @@ enum fusedops_dtype {
  *                     F8E4M3. Absent: sa = 1.
  *   DEQUANT_COL       in = sw (fp32, length N): the weight scale of each output channel (row of W).
  *                     Requires in_dtype = F8E4M3. Absent: sw = 1.
+ *   ROW_RMS           The row scale of the deferred RMSNorm, computed by the kernel itself: in =
+ *                     partials (fp32, M x T, row stride ld >= T) as a previous call's ROWSUMSQ_PARTIAL
+ *                     wrote them for rows of width d, n_split = d (T = ceil(d / 128)), reserved = the
+ *                     bit pattern of eps (fp32, > 0). r[m] = 1 / sqrt(sum_t p[m,t] / d + eps), the
+ *                     formula of fusedops_rmsnorm_finalize, then used as ROW_SCALE's r: the light
+ *                     reduction runs inside this GEMM, overlapping its mainloop ([Epilogue] §模式A,
+ *                     Fig. 4). Not combinable with ROW_SCALE.
  *   ROPE              in = table (fp32, M rows, row stride ld >= d floats), n_split = d (head width,
  *                     a multiple of 8). Column pair (2j, 2j+1) of output row m, with i = (2j mod d)/2,
  *                     becomes (a c - b s, a s + b c) where c = table[m][2i], s = table[m][2i+1]: row
@@ -123,7 +130,8 @@ enum fusedops_op_kind {
   FUSEDOPS_OP_SPLIT_COLS = 10,
   FUSEDOPS_OP_DEQUANT_ROW = 11,
   FUSEDOPS_OP_DEQUANT_COL = 12,
-  FUSEDOPS_OP_ROPE = 13
+  FUSEDOPS_OP_ROPE = 13,
+  FUSEDOPS_OP_ROW_RMS = 14
 };
 
 enum fusedops_gelu_form {
@@ -141,7 +149,7 @@ typedef struct fusedops_op {
   int64_t ld;         /* row stride of a 2-D `in` / `out` / out_v block, in elements */
   void* out_v[3];     /* SPLIT_COLS destinations */
   int32_t n_split;    /* SPLIT_COLS block count */
-  int32_t reserved;   /* must be 0 */
+  int32_t reserved;   /* 0, except ROW_RMS: the fp32 bit pattern of eps */
 } fusedops_op;
 
 /*

@@ -118,6 +118,24 @@ def test_rope_rules():
     assert lin(N=96, Y=None, ops=[split, rope(48)]) == B.ERR_INVALID_ARG  # Q+K width 64 vs d = 48
 
 
+def test_row_rms_rules():
+    import struct
+    def rms(width=64, eps=1e-6, ld=1, inp=addr(7)):
+        o = mkop(B.OP_ROW_RMS, dtype=B.F32, inp=inp, ld=ld)
+        o.n_split = width
+        o.reserved = int.from_bytes(struct.pack("<f", eps), "little", signed=True)
+        return o
+    assert lin(ops=[rms(eps=0.0)]) == B.ERR_INVALID_ARG                 # eps must be > 0
+    assert lin(ops=[rms(eps=float("inf"))]) == B.ERR_INVALID_ARG
+    assert lin(ops=[rms(width=0)]) == B.ERR_INVALID_ARG
+    assert lin(ops=[rms(width=300, ld=2)]) == B.ERR_INVALID_ARG         # ld < ceil(300 / 128)
+    assert lin(ops=[rms(inp=None)]) == B.ERR_INVALID_ARG
+    assert lin(ops=[mkop(B.OP_ROW_SCALE, dtype=B.F32, inp=addr(6)), rms()]) == B.ERR_INVALID_ARG  # both scales
+    assert lin(ops=[rms(inp=addr(7, 2))]) == B.ERR_MISALIGNED
+    assert lin(ops=[rms(inp=addr(2))]) == B.ERR_INVALID_ARG             # partials overlap Y
+    assert lin(ops=[mkop(B.OP_GELU_ERF, reserved=7)]) == B.ERR_INVALID_ARG  # reserved only for ROW_RMS
+
+
 def test_op_list_rules():
     gelu, tanh, sw = mkop(B.OP_GELU_ERF), mkop(B.OP_GELU_TANH), mkop(B.OP_SWIGLU)
     res = mkop(B.OP_RESIDUAL_ADD, inp=addr(5), ld=64)

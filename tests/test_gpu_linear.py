@@ -454,3 +454,60 @@ def test_finalize_apply_mode():
     check_f32(host64(r), r_ref, "r")
     check_lowp(host64(y.view), O.rmsnorm_apply(r_ref, I.to_f64(h, I.BF16), I.to_f64(g, I.BF16)), "applied")
     assert y.intact()
+
+
+# ---------------------------------------------------------------------------
+# pattern A chained: out-projection epilogue -> deferred RMSNorm row scale computed inside the
+# gate/up GEMM from the row partials (ROW_RMS) -> SwiGLU
+# ---------------------------------------------------------------------------
+
+def run_pattern_a(M, d, K0, N2, *, act="swiglu", out_dtype=I.BF16, eps=1e-6, seed=0):
+    rng = np.random.default_rng([202, M, d, K0, N2, seed])
+    X = I.random_stored(rng, (M, K0), I.BF16)
+    W0 = I.random_stored(rng, (d, K0), I.BF16, std=1 / math.sqrt(K0))
+    z = I.random_stored(rng, (M, d), I.BF16)
+    g = I.random_stored(rng, (d,), I.BF16, mean=1.0, std=0.1)
+    W1 = I.random_stored(rng, (N2, d), I.BF16, std=1 / math.sqrt(d))
+    note(f"pattern A M={M} d={d} K0={K0} N2={N2} act={act} out={out_dtype}")
+    T = -(-d // 128)
+    zd, gd = dev(z, I.BF16), dev(g, I.BF16)
+    h1 = Guarded(M, d, I.BF16)
+    p = Guarded(M, T, I.F32, ld=T + 3)
+    h2 = torch.empty((M, d), dtype=torch.bfloat16, device="cuda")
+    ops1 = [B.op(B.OP_RESIDUAL_ADD, zd), B.op(B.OP_STORE_AUX, out=h1.view), B.op(B.OP_ROWSUMSQ_PARTIAL, out=p.view),
+            B.op(B.OP_COL_SCALE, gd)]
+    st = B.fusedops_linear_epilogue(dev(X, I.BF16), dev(W0, I.BF16), h2, ops=ops1)
+    assert st == B.OK, B.status_string(st)
+    n_out = N2 // 2 if act == "swiglu" else N2
+    y = Guarded(M, n_out, out_dtype)
+    ops2 = ([B.op(ACT_OP[act])] if act else []) + [B.row_rms_op(p.view, d, eps)]  # increasing kind order
+    st = B.fusedops_linear_epilogue(h2, dev(W1, I.BF16), y.view, ops=ops2, out_dtype=out_dtype)
+    assert st == B.OK, B.status_string(st)
+    torch.cuda.synchronize()
+    assert h1.intact() and p.intact() and y.intact()
+    ref = O.pattern_a_chain(I.to_f64(X, I.BF16), I.to_f64(W0, I.BF16), I.to_f64(z, I.BF16), I.to_f64(g, I.BF16),
+                            I.to_f64(W1, I.BF16), eps, act=act, h2_stored=host64(h2))
+    check_out(host64(h1.view), ref["h1"], I.BF16, "h1")
+    check_f32(host64(p.view), ref["partials"], "partials")
+    check_out(host64(h2), ref["h2"], I.BF16, "h2")
+    check_out(host64(y.view), ref["y"], out_dtype, "y")
+    return {"h2": h2, "p": p, "y": y, "W1": W1}
+
+
+@pytest.mark.parametrize("M,d,K0,N2", [(300, 264, 136, 528), (70, 256, 64, 512)])
+def test_pattern_a_row_rms_swiglu(M, d, K0, N2):
+    run_pattern_a(M, d, K0, N2)
+
+
+def test_pattern_a_generic_chain_and_finalize_equivalence():
+    out = run_pattern_a(300, 264, 136, 264, act="gelu_erf", out_dtype=I.F32)
+    # the same GEMM with ROW_SCALE(r) from the finalize kernel: r agrees to fp32 rounding
+    M, d = 300, 264
+    r = torch.empty(M, dtype=torch.float32, device="cuda")
+    assert B.fusedops_rmsnorm_finalize(out["p"].view, d, 1e-6, r) == B.OK
+    y2 = torch.empty((M, 264), dtype=torch.float32, device="cuda")
+    st = B.fusedops_linear_epilogue(out["h2"], dev(out["W1"], I.BF16), y2, ops=[B.op(B.OP_ROW_SCALE, r),
+                                                                              B.op(B.OP_GELU_ERF)])
+    assert st == B.OK
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host64(y2), host64(out["y"].view), rtol=2e-6, atol=1e-6)
