@@ -49,9 +49,10 @@ SUITE = [
     ("linear_gelu_f32_64x256x256", "latency"),
 ]
 DOMINANT = "mlp_up_gelu_bf16_8192x16384x4096"
-# Widening beyond the suite above (RoPE, E4M3 inputs): timed and reported under "next_workloads",
+# Widening beyond the suite above (the pattern-A chain, RoPE, E4M3 inputs): timed and reported under "next_workloads",
 # each against the fp8 MFMA peak, and not part of `value`.
 NEXT = [
+    ("chain_outproj_gateup_rms_bf16_16384x2048x16384", "mfma"),
     ("qkv_bias_rope_split_bf16_4096x12288x4096", "mfma"),
     ("downproj_residual_fp8in_16384x2048x8192", "mfma"),
     ("mlp_up_gelu_fp8in_8192x16384x4096", "mfma"),
@@ -79,6 +80,8 @@ def copies_for(spec) -> int:
     from gelu_bf16_gemm_amd import inputs as I
     if spec["kind"] == "ln":
         per = spec["rows"] * spec["cols"] * 2
+    elif spec["kind"] == "chain":
+        per = (spec["M"] * spec["K0"] + spec["M"] * spec["d"]) * 2
     else:
         es = {I.F32: 4, I.F8E4M3: 1}.get(spec["in_dtype"], 2)
         per = (spec["M"] + spec["N"]) * spec["K"] * es + (spec["M"] * spec["N"] * 2 if spec.get("residual") else 0)
@@ -192,6 +195,8 @@ def main() -> int:
         print(f"[bench] {name}: inputs", file=sys.stderr, flush=True)
         if spec["kind"] == "ln":
             run = WL.LnRun(spec, I.make_ln_inputs(spec), copies=copies_for(spec))
+        elif spec["kind"] == "chain":
+            run = WL.ChainRun(spec, I.make_chain_inputs(spec), copies=copies_for(spec))
         else:
             run = WL.LinearRun(spec, I.make_linear_inputs(spec), copies=copies_for(spec))
         print(f"[bench] {name}: timing", file=sys.stderr, flush=True)

@@ -113,6 +113,11 @@ WORKLOADS = {
     "prefill_swiglu_fp8_bf16_16384x16384x2048": dict(config_id=9, kind="linear", M=16384, N=16384,
                                                      K=2048, in_dtype=BF16, bias=False, act="swiglu",
                                                      quant_fp8=True, out_dtype=F8E4M3),
+    # Pattern A end to end: the out-projection of config 6 (residual, h1, partials, gamma -> h2)
+    # feeding the gate/up layer of config 7, whose epilogue applies the deferred RMSNorm row scale
+    # computed from the partials (ROW_RMS) before SwiGLU.
+    "chain_outproj_gateup_rms_bf16_16384x2048x16384": dict(config_id=13, kind="chain", M=16384, d=2048,
+                                                           K0=2048, N2=16384, eps=1e-6, act="swiglu"),
     # The fused QKV projection with RoPE on its Q and K blocks (head width 128).
     "qkv_bias_rope_split_bf16_4096x12288x4096": dict(config_id=12, kind="linear", M=4096, N=12288,
                                                      K=4096, in_dtype=BF16, bias=True, act=None,
@@ -129,7 +134,7 @@ WORKLOADS = {
 }
 
 # tensor ids inside one config
-_T_X, _T_W, _T_B, _T_Z, _T_GAMMA, _T_BETA, _T_SA, _T_SW, _T_ROPE = 0, 1, 2, 3, 4, 5, 6, 7, 8
+_T_X, _T_W, _T_B, _T_Z, _T_GAMMA, _T_BETA, _T_SA, _T_SW, _T_ROPE, _T_W1 = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 def random_e4m3_codes(rng: np.random.Generator, shape, e_lo: int = 4, e_hi: int = 10) -> np.ndarray:
@@ -179,6 +184,19 @@ def make_linear_inputs(spec: dict, seed: int = 0, M: int | None = None, N: int |
         cs[:, 0::2], cs[:, 1::2] = np.cos(ang), np.sin(ang)
         out["rope_cs"] = cs
     return out
+
+
+def make_chain_inputs(spec: dict, seed: int = 0) -> dict:
+    """X (M, K0) ~ N(0,1); W0 (d, K0) var 1/K0; z (M, d) ~ N(0,1); gamma = 1 + N(0, std 0.1);
+    W1 (N2, d) var 1/d; all bf16."""
+    cid, M, d, K0, N2 = spec["config_id"], spec["M"], spec["d"], spec["K0"], spec["N2"]
+    return {
+        "X": store(normal(rng_for(cid, _T_X, seed), (M, K0)), BF16),
+        "W0": store(normal(rng_for(cid, _T_W, seed), (d, K0), std=float(1.0 / np.sqrt(K0))), BF16),
+        "z": store(normal(rng_for(cid, _T_Z, seed), (M, d)), BF16),
+        "gamma": store(normal(rng_for(cid, _T_GAMMA, seed), (d,), mean=1.0, std=0.1), BF16),
+        "W1": store(normal(rng_for(cid, _T_W1, seed), (N2, d), std=float(1.0 / np.sqrt(d))), BF16),
+    }
 
 
 def make_ln_inputs(spec: dict, seed: int = 0, rows: int | None = None, cols: int | None = None) -> dict:

@@ -165,6 +165,55 @@ class LinearRun:
         return float(b)
 
 
+class ChainRun:
+    """Pattern A end to end: GEMM 1 (residual, h1, row partials, gamma) writes h2; GEMM 2 reads
+    h2 and applies the deferred RMSNorm row scale from the partials (ROW_RMS) before its
+    activation. One pass = both launches."""
+
+    def __init__(self, spec: dict, inp: dict, copies: int = 1):
+        self.spec = spec
+        M, d, K0, N2 = spec["M"], spec["d"], spec["K0"], spec["N2"]
+        self.M, self.d, self.K0, self.N2 = M, d, K0, N2
+        self.copies = copies
+        dev = "cuda"
+        self.X = [to_device(inp["X"], I.BF16) for _ in range(copies)]
+        self.W0 = to_device(inp["W0"], I.BF16)
+        self.z = [to_device(inp["z"], I.BF16) for _ in range(copies)]
+        self.gamma = to_device(inp["gamma"], I.BF16)
+        self.W1 = to_device(inp["W1"], I.BF16)
+        T = -(-d // 128)
+        self.h1 = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+        self.partials = torch.empty((M, T), dtype=torch.float32, device=dev)
+        self.h2 = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+        self.n_out = N2 // 2 if spec["act"] == "swiglu" else N2
+        self.y = torch.empty((M, self.n_out), dtype=torch.bfloat16, device=dev)
+        self.ops1 = [[B.op(B.OP_RESIDUAL_ADD, self.z[i]), B.op(B.OP_STORE_AUX, out=self.h1),
+                      B.op(B.OP_ROWSUMSQ_PARTIAL, out=self.partials), B.op(B.OP_COL_SCALE, self.gamma)]
+                     for i in range(copies)]
+        act = {"swiglu": B.OP_SWIGLU, "gelu_erf": B.OP_GELU_ERF}[spec["act"]]
+        self.ops2 = [B.op(act), B.row_rms_op(self.partials, d, spec["eps"])]
+
+    def launch(self, i: int = 0, stream=None) -> None:
+        i %= self.copies
+        B.check(B.fusedops_linear_epilogue(self.X[i], self.W0, self.h2, ops=self.ops1[i], stream=stream))
+        B.check(B.fusedops_linear_epilogue(self.h2, self.W1, self.y, ops=self.ops2, stream=stream))
+
+    def outputs(self, rows) -> dict:
+        idx = torch.as_tensor(np.asarray(rows), device="cuda")
+        return {k: _host64(getattr(self, k).index_select(0, idx)) for k in ("h1", "partials", "h2", "y")}
+
+    def flops(self) -> float:
+        return 2.0 * self.M * self.d * self.K0 + 2.0 * self.M * self.N2 * self.d
+
+    def bytes(self) -> float:
+        """HBM bytes the chain must move: inputs once, h1 / h2 / partials written once and h2 and
+        the partials read once more by the second GEMM, y written once."""
+        M, d, K0, N2 = self.M, self.d, self.K0, self.N2
+        T = -(-d // 128)
+        return float(2 * (M * K0 + d * K0 + M * d + d + N2 * d) + 2 * M * d * 2 + M * T * 4 * 2
+                     + 2 * M * d + 2 * M * self.n_out)
+
+
 class LnRun:
     """The LayerNorm+GELU row workload."""
 

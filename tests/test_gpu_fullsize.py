@@ -72,6 +72,26 @@ def test_linear_workload_full_size(name):
         check_f32(out["r"], O.rmsnorm_finalize(ref["partials"], spec["N"], spec["eps"]), f"{name} r")
 
 
+@pytest.mark.parametrize("name", [n for n, s in I.WORKLOADS.items() if s["kind"] == "chain"])
+def test_chain_workload_full_size(name):
+    spec = I.WORKLOADS[name]
+    note(f"full-size {name}: drawing inputs")
+    inp = I.make_chain_inputs(spec)
+    run = WL.ChainRun(spec, inp)
+    note(f"full-size {name}: launch")
+    run.launch()
+    torch.cuda.synchronize()
+    rows = sample_rows(spec["M"])
+    out = run.outputs(rows)
+    ref = O.pattern_a_chain(I.to_f64(inp["X"][rows], I.BF16), I.to_f64(inp["W0"], I.BF16),
+                            I.to_f64(inp["z"][rows], I.BF16), I.to_f64(inp["gamma"], I.BF16),
+                            I.to_f64(inp["W1"], I.BF16), spec["eps"], act=spec["act"], h2_stored=out["h2"])
+    check_out(out["h1"], ref["h1"], I.BF16, f"{name} h1")
+    check_f32(out["partials"], ref["partials"], f"{name} partials")
+    check_out(out["h2"], ref["h2"], I.BF16, f"{name} h2")
+    check_out(out["y"], ref["y"], I.BF16, f"{name} y")
+
+
 @pytest.mark.parametrize("name", [n for n, s in I.WORKLOADS.items() if s["kind"] == "ln"])
 def test_layernorm_workload_full_size(name):
     spec = I.WORKLOADS[name]
