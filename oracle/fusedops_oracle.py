@@ -52,6 +52,7 @@ __all__ = [
     "merge_sumsq", "merge_absmax", "merge_mean_m2", "merge_max_sumexp",
     "e4m3_values", "e4m3_decode", "e4m3_encode", "e4m3_ordinal",
     "fp8_row_scale", "quantize_fp8_rows", "split_cols", "rope_pairs", "rope_table", "pattern_a_chain",
+    "cross_entropy", "xent_chunk_stats", "xent_merge_loss",
 ]
 
 PARTIAL_COLS = 128          # public granularity of the RMSNorm row partials
@@ -356,6 +357,50 @@ def merge_max_sumexp(a, b):
     m2, s2 = b
     m = np.maximum(m1, m2)
     return m, s1 * np.exp(m1 - m) + s2 * np.exp(m2 - m)
+
+
+# ---------------------------------------------------------------------------
+# Cross-entropy over the output columns (a stateful epilogue plus a final merge)
+# ---------------------------------------------------------------------------
+
+def cross_entropy(h: np.ndarray, labels) -> np.ndarray:
+    """l[i] = -h[i, y_i] + log sum_k exp(h[i, k]) ([Epilogue] §模式C); rows whose label is
+    outside [0, N) are ignored (loss 0). The log-sum-exp is taken around the row maximum."""
+    h = np.asarray(h, dtype=np.float64)
+    lab = np.asarray(labels, dtype=np.int64)
+    mx = h.max(axis=1)
+    lse = mx + np.log(np.exp(h - mx[:, None]).sum(axis=1))
+    ok = (lab >= 0) & (lab < h.shape[1])
+    tgt = np.where(ok, h[np.arange(h.shape[0]), np.clip(lab, 0, h.shape[1] - 1)], 0.0)
+    return np.where(ok, lse - tgt, 0.0)
+
+
+def xent_chunk_stats(h: np.ndarray, chunk: int = PARTIAL_COLS):
+    """Per row and per `chunk`-column block t: m[i,t] = max_j h[i,j], s[i,t] = sum_j e^(h[i,j]-m[i,t])
+    over the block's columns (the per-tile running statistics of [Epilogue] §模式C)."""
+    h = np.asarray(h, dtype=np.float64)
+    M, N = h.shape
+    T = -(-N // chunk)
+    m = np.empty((M, T))
+    s = np.empty((M, T))
+    for t in range(T):
+        blk = h[:, t * chunk:(t + 1) * chunk]
+        m[:, t] = blk.max(axis=1)
+        s[:, t] = np.exp(blk - m[:, t][:, None]).sum(axis=1)
+    return m, s
+
+
+def xent_merge_loss(m: np.ndarray, s: np.ndarray, target, labels, n_cols: int) -> np.ndarray:
+    """The final merge along the vocabulary: fold the chunks' (m, s) with merge_max_sumexp, then
+    l = m + log s - target for rows with a label in [0, n_cols), 0 otherwise."""
+    m = np.asarray(m, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    acc = (m[:, 0], s[:, 0])
+    for t in range(1, m.shape[1]):
+        acc = merge_max_sumexp(acc, (m[:, t], s[:, t]))
+    lab = np.asarray(labels, dtype=np.int64)
+    ok = (lab >= 0) & (lab < n_cols)
+    return np.where(ok, acc[0] + np.log(acc[1]) - np.asarray(target, dtype=np.float64), 0.0)
 
 
 # ---------------------------------------------------------------------------

@@ -256,6 +256,45 @@ def test_pattern_a_equals_normalising_before_the_second_gemm(act):
     np.testing.assert_allclose(out["r"], 1.0 / np.sqrt((h1 * h1).mean(axis=1) + 1e-6), rtol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# cross-entropy epilogue
+# ---------------------------------------------------------------------------
+
+def test_cross_entropy_closed_forms():
+    N = 37
+    assert np.allclose(O.cross_entropy(np.zeros((2, N)), [0, 36]), math.log(N), rtol=0, atol=1e-14)  # uniform
+    h = np.zeros((1, N))
+    h[0, 5] = 60.0
+    # the exact loss 36 e^-60 ~ 3e-25 is below the fp64 resolution of lse ~ 60 (about 1e-14)
+    assert O.cross_entropy(h, [5])[0] == pytest.approx((N - 1) * math.exp(-60.0), abs=1e-13)
+    assert O.cross_entropy(h, [4])[0] == pytest.approx(60.0, rel=1e-12)
+    assert O.cross_entropy(h, [-100])[0] == 0.0 and O.cross_entropy(h, [N])[0] == 0.0   # ignored rows
+    # two classes: -log sigmoid of the margin
+    assert O.cross_entropy(np.array([[1.5, -0.5]]), [0])[0] == pytest.approx(math.log1p(math.exp(-2.0)), rel=1e-14)
+
+
+def test_cross_entropy_brute_force_and_shift_invariance():
+    rng = np.random.default_rng(51)
+    h = rng.standard_normal((4, 9)) * 3
+    lab = [0, 8, 3, 5]
+    want = [-h[i, lab[i]] + math.log(sum(math.exp(v) for v in h[i])) for i in range(4)]
+    np.testing.assert_allclose(O.cross_entropy(h, lab), want, rtol=1e-13)
+    np.testing.assert_allclose(O.cross_entropy(h + 700.0, lab), want, rtol=1e-11)   # no overflow
+
+
+@pytest.mark.parametrize("N,chunk", [(1000, 128), (128, 128), (300, 64), (5, 128)])
+def test_xent_chunk_stats_merge_to_the_direct_loss(N, chunk):
+    rng = np.random.default_rng([52, N, chunk])
+    M = 6
+    h = rng.standard_normal((M, N)) * 4
+    lab = rng.integers(-1, N, size=M)
+    m, s = O.xent_chunk_stats(h, chunk)
+    assert m.shape == (M, -(-N // chunk))
+    assert np.all(s >= 1.0)            # the chunk maximum contributes e^0 = 1
+    tgt = h[np.arange(M), np.clip(lab, 0, N - 1)]
+    np.testing.assert_allclose(O.xent_merge_loss(m, s, tgt, lab, N), O.cross_entropy(h, lab), rtol=1e-12, atol=1e-12)
+
+
 def test_gelu_erf_textbook_normal_cdf():
     for x, phi in _load_cdf():
         assert O.gelu_erf(np.array([x]))[0] == pytest.approx(x * phi, rel=1e-15, abs=1e-16)
