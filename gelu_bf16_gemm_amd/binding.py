@@ -35,15 +35,16 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_LAUNCH 
 F32, BF16, F16, F8E4M3 = 0, 1, 2, 3
 (OP_RESIDUAL_ADD, OP_STORE_AUX, OP_ROWSUMSQ_PARTIAL, OP_COL_SCALE, OP_ROW_SCALE, OP_GELU_ERF,
  OP_GELU_TANH, OP_SWIGLU, OP_QUANT_FP8_ROW, OP_SPLIT_COLS, OP_DEQUANT_ROW, OP_DEQUANT_COL, OP_ROPE,
- OP_ROW_RMS) = range(1, 15)
+ OP_ROW_RMS, OP_XENT) = range(1, 16)
 GELU_NONE, GELU_TANH, GELU_ERF = 0, 1, 2
 PARTIAL_COLS = 128
+XENT_COLS = 64
 LN_MAX_COLS = 16384
 
 # every symbol the public header declares
 EXPORTS = ("fusedops_linear_epilogue", "fusedops_linear_workspace_bytes", "fusedops_layernorm_gelu",
-           "fusedops_rmsnorm_finalize", "fusedops_partial_cols", "fusedops_abi_version",
-           "fusedops_status_string")
+           "fusedops_rmsnorm_finalize", "fusedops_cross_entropy_finalize", "fusedops_partial_cols",
+           "fusedops_abi_version", "fusedops_status_string")
 
 
 class Op(ctypes.Structure):
@@ -68,6 +69,8 @@ lib.fusedops_layernorm_gelu.argtypes = [_vp, _i64, _vp, _i64, _i64, _i64, _i32, 
 lib.fusedops_rmsnorm_finalize.restype = _i32
 lib.fusedops_rmsnorm_finalize.argtypes = [_vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _i64, _vp,
                                           _vp, _i64, _i32, _vp]
+lib.fusedops_cross_entropy_finalize.restype = _i32
+lib.fusedops_cross_entropy_finalize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
 lib.fusedops_partial_cols.restype = _i32
 lib.fusedops_partial_cols.argtypes = []
 lib.fusedops_abi_version.restype = _i32
@@ -196,6 +199,24 @@ def fusedops_rmsnorm_finalize(partials, n_cols: int, eps: float, r, *, h=None, g
         partials.data_ptr(), _ld(partials), M, T, n_cols, eps, r.data_ptr(), _ptr(h),
         _ld(h) if h is not None else 0, _ptr(gamma), _ptr(y), _ld(y) if y is not None else 0, dt,
         _stream(stream))
+
+
+def xent_op(labels, stats, target) -> Op:
+    """XENT: labels (int32, M), stats (fp32, M x 2T), target (fp32, M)."""
+    o = Op()
+    o.kind = OP_XENT
+    o.dtype = F32
+    o.in_ = labels.data_ptr()
+    o.out = stats.data_ptr()
+    o.ld = _ld(stats)
+    o.out_v[0] = target.data_ptr()
+    return o
+
+
+def fusedops_cross_entropy_finalize(stats, n_cols: int, target, labels, loss, *, stream=None) -> int:
+    M = stats.shape[0]
+    return lib.fusedops_cross_entropy_finalize(stats.data_ptr(), _ld(stats), M, n_cols, target.data_ptr(),
+                                               labels.data_ptr(), loss.data_ptr(), _stream(stream))
 
 
 def abi_version() -> int:

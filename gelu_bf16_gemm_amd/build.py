@@ -23,6 +23,7 @@ SOURCES = [
     "gemm_f32.hip",
     "layernorm_gelu.hip",
     "rmsnorm_finalize.hip",
+    "xent_finalize.hip",
     "api.cpp",
 ]
 

@@ -36,6 +36,7 @@ constexpr uint32_t kBias = 1u << 0, kZ = 1u << 1, kAux = 1u << 2, kPart = 1u << 
                    kRscale = 1u << 5, kQuant = 1u << 6, kSplit = 1u << 7;
 // op lists with a RoPE rotation have no instance of their own (the generic one runs them)
 constexpr uint32_t kRope = 1u << 20;
+constexpr uint32_t kXent = 1u << 21;  // so do op lists with cross-entropy statistics
 constexpr int kActShift = 8, kYShift = 10, kZShift = 12, kAuxShift = 14, kBiasShift = 16, kGammaShift = 18;
 
 constexpr uint32_t config(uint32_t ops, int act, int y_dtype, int z_dtype = FUSEDOPS_BF16,
@@ -58,6 +59,7 @@ __host__ __device__ inline uint32_t config_of(const EpiParams& e) {
   if (e.quant) ops |= kQuant;
   if (e.n_split) ops |= kSplit;
   if (e.rope_cs) ops |= kRope;
+  if (e.xent_labels) ops |= kXent;
   return config(ops, e.act, e.y_dtype, e.z ? e.z_dtype : FUSEDOPS_BF16, e.aux ? e.aux_dtype : FUSEDOPS_BF16,
                 e.bias ? e.bias_dtype : FUSEDOPS_BF16, e.gamma ? e.gamma_dtype : FUSEDOPS_BF16);
 }

@@ -52,7 +52,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Parsed epilogue op list.
 struct OpList {
-  const fusedops_op* by_kind[15] = {};
+  const fusedops_op* by_kind[16] = {};
   int act = ACT_NONE;
   bool quant = false;
 };
@@ -63,7 +63,7 @@ int32_t parse_ops(const fusedops_op* ops, int32_t n_ops, OpList& out) {
   int n_act = 0;
   for (int i = 0; i < n_ops; ++i) {
     const fusedops_op& op = ops[i];
-    if (op.kind < FUSEDOPS_OP_RESIDUAL_ADD || op.kind > FUSEDOPS_OP_ROW_RMS) return FUSEDOPS_ERR_INVALID_ARG;
+    if (op.kind < FUSEDOPS_OP_RESIDUAL_ADD || op.kind > FUSEDOPS_OP_XENT) return FUSEDOPS_ERR_INVALID_ARG;
     if (op.kind <= last) return FUSEDOPS_ERR_INVALID_ARG;  // increasing kind order, each kind once
     if (op.reserved != 0 && op.kind != FUSEDOPS_OP_ROW_RMS) return FUSEDOPS_ERR_INVALID_ARG;
     last = op.kind;
@@ -153,6 +153,8 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   const fusedops_op* op_dqc = ol.by_kind[FUSEDOPS_OP_DEQUANT_COL];
   const fusedops_op* op_rope = ol.by_kind[FUSEDOPS_OP_ROPE];
   const fusedops_op* op_rms = ol.by_kind[FUSEDOPS_OP_ROW_RMS];
+  const fusedops_op* op_xe = ol.by_kind[FUSEDOPS_OP_XENT];
+  const int64_t xent_T = cdiv(N, FUSEDOPS_XENT_COLS);
   float rms_eps = 0.f;
   if (op_rms) std::memcpy(&rms_eps, &op_rms->reserved, sizeof(float));
   const int64_t rms_T = op_rms ? cdiv(op_rms->n_split, FUSEDOPS_PARTIAL_COLS) : 0;
@@ -176,7 +178,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
     for (int i = 0; i < op_split->n_split; ++i)
       if (!op_split->out_v[i]) return FUSEDOPS_ERR_INVALID_ARG;
     if (N % op_split->n_split) return FUSEDOPS_ERR_INVALID_ARG;
-  } else if (!Y) {
+  } else if (!Y && !op_xe) {
     return FUSEDOPS_ERR_INVALID_ARG;
   }
   const int es_out = dtype_size(out_dtype);
@@ -190,6 +192,10 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (op_q && !op_q->out) return FUSEDOPS_ERR_INVALID_ARG;
   if ((op_dqr || op_dqc) && !fp8_in) return FUSEDOPS_ERR_INVALID_ARG;  // scales of FP8 inputs only
   if ((op_dqr && !op_dqr->in) || (op_dqc && !op_dqc->in)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (op_xe) {
+    if (!op_xe->in || !op_xe->out || !op_xe->out_v[0] || op_xe->ld < 2 * xent_T) return FUSEDOPS_ERR_INVALID_ARG;
+    if (swiglu || ol.quant || op_split) return FUSEDOPS_ERR_INVALID_ARG;
+  }
   if (op_rms) {
     if (op_row || !op_rms->in || op_rms->n_split < 1 || op_rms->ld < rms_T) return FUSEDOPS_ERR_INVALID_ARG;
     if (!(rms_eps > 0.f) || !std::isfinite(rms_eps)) return FUSEDOPS_ERR_INVALID_ARG;
@@ -221,6 +227,8 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if ((op_dqr && !aligned(op_dqr->in, 4)) || (op_dqc && !aligned(op_dqc->in, 4))) return FUSEDOPS_ERR_MISALIGNED;
   if (op_rope && (!aligned(op_rope->in, 16) || op_rope->ld % 4)) return FUSEDOPS_ERR_MISALIGNED;
   if (op_rms && !aligned(op_rms->in, 4)) return FUSEDOPS_ERR_MISALIGNED;
+  if (op_xe && (!aligned(op_xe->in, 4) || !aligned(op_xe->out, 4) || !aligned(op_xe->out_v[0], 4)))
+    return FUSEDOPS_ERR_MISALIGNED;
   if (op_split) {
     if ((N / op_split->n_split) % 8) return FUSEDOPS_ERR_MISALIGNED;
     if ((op_split->ld * es_out) % 16) return FUSEDOPS_ERR_MISALIGNED;
@@ -229,7 +237,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   }
 
   // ---- aliasing: outputs may not overlap inputs or each other, except Y == z exactly
-  constexpr int kInSpans = 10;
+  constexpr int kInSpans = 11;
   Span in_spans[kInSpans] = {
       span2d(X, M, K, ldx, es_in), span2d(W, N, K, ldw, es_in), span2d(bias, 1, N, N, dtype_size(bias_dtype)),
       op_res ? span2d(op_res->in, M, N, op_res->ld, dtype_size(op_res->dtype)) : Span{},
@@ -238,8 +246,9 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
       op_dqr ? span2d(op_dqr->in, 1, M, M, 4) : Span{},
       op_dqc ? span2d(op_dqc->in, 1, N, N, 4) : Span{},
       op_rope ? span2d(op_rope->in, M, op_rope->n_split, op_rope->ld, 4) : Span{},
-      op_rms ? span2d(op_rms->in, M, rms_T, op_rms->ld, 4) : Span{}};
-  Span out_spans[6];
+      op_rms ? span2d(op_rms->in, M, rms_T, op_rms->ld, 4) : Span{},
+      op_xe ? span2d(op_xe->in, 1, M, M, 4) : Span{}};
+  Span out_spans[10];
   int n_out_spans = 0;
   if (Y) out_spans[n_out_spans++] = span2d(Y, M, n_out, ldy, es_out);
   if (op_split)
@@ -248,6 +257,10 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (op_aux) out_spans[n_out_spans++] = span2d(op_aux->out, M, N, op_aux->ld, dtype_size(op_aux->dtype));
   if (op_par) out_spans[n_out_spans++] = span2d(op_par->out, M, T, op_par->ld, 4);
   if (op_q) out_spans[n_out_spans++] = span2d(op_q->out, 1, M, M, 4);
+  if (op_xe) {
+    out_spans[n_out_spans++] = span2d(op_xe->out, M, 2 * xent_T, op_xe->ld, 4);
+    out_spans[n_out_spans++] = span2d(op_xe->out_v[0], 1, M, M, 4);
+  }
   const bool y_is_z = Y && op_res && Y == op_res->in && ldy == op_res->ld && out_dtype == op_res->dtype &&
                       !swiglu;
   for (int o = 0; o < n_out_spans; ++o) {
@@ -301,6 +314,12 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   e.bias = bias; e.bias_dtype = bias_dtype;
   if (op_dqr) e.dq_row = static_cast<const float*>(op_dqr->in);
   if (op_dqc) e.dq_col = static_cast<const float*>(op_dqc->in);
+  if (op_xe) {
+    e.xent_labels = static_cast<const int*>(op_xe->in);
+    e.xent_stats = static_cast<float*>(op_xe->out);
+    e.xent_ld = op_xe->ld;
+    e.xent_tgt = static_cast<float*>(op_xe->out_v[0]);
+  }
   if (op_rms) {
     e.rms_p = static_cast<const float*>(op_rms->in);
     e.rms_ldp = op_rms->ld;
@@ -432,6 +451,22 @@ int32_t fusedops_rmsnorm_finalize(const float* partials, int64_t ldp, int64_t M,
   a.partials = partials; a.ldp = ldp; a.M = M; a.T = (int)T; a.N = N; a.eps = eps; a.r = r;
   a.h = h; a.ldh = ldh; a.gamma = gamma; a.y = y; a.ldy = ldy; a.dtype = dtype;
   return launch_status(launch_rmsnorm_finalize(a, static_cast<hipStream_t>(stream)), "rmsnorm_finalize");
+}
+
+int32_t fusedops_cross_entropy_finalize(const float* stats, int64_t ld, int64_t M, int64_t n_cols,
+                                        const float* target, const int32_t* labels, float* loss,
+                                        void* stream) {
+  if (!stats || !target || !labels || !loss || M < 1 || n_cols < 1) return FUSEDOPS_ERR_INVALID_ARG;
+  const int64_t T = cdiv(n_cols, FUSEDOPS_XENT_COLS);
+  if (ld < 2 * T || M > (int64_t(1) << 31) || n_cols > (int64_t(1) << 31)) return FUSEDOPS_ERR_INVALID_ARG;
+  if (!aligned(stats, 4) || !aligned(target, 4) || !aligned(labels, 4) || !aligned(loss, 4))
+    return FUSEDOPS_ERR_MISALIGNED;
+  const Span out = span2d(loss, 1, M, M, 4);
+  if (overlap(out, span2d(stats, M, 2 * T, ld, 4)) || overlap(out, span2d(target, 1, M, M, 4)) ||
+      overlap(out, span2d(labels, 1, M, M, 4)))
+    return FUSEDOPS_ERR_INVALID_ARG;
+  XentFinalizeArgs a{stats, ld, M, T, n_cols, target, labels, loss};
+  return launch_status(launch_xent_finalize(a, static_cast<hipStream_t>(stream)), "xent_finalize");
 }
 
 }  // extern "C"

@@ -39,6 +39,10 @@ struct EpiParams {
   int rms_T;              //   partials per row
   int rms_n;              //   width the partials cover
   float rms_eps;
+  const int* xent_labels; // XENT: label per row (null: no cross-entropy statistics)
+  float* xent_stats;      //   (max, sum-exp) per row and 64-column chunk
+  int64_t xent_ld;        //   row stride of the statistics
+  float* xent_tgt;        //   y at the label, per row
   const float* rope_cs;   // RoPE: per-row cos / sin table (null: no rotation)
   int64_t rope_ld;        //   its row stride in floats
   int rope_d;             //   head width (pair index i = (column mod d) / 2)
@@ -368,10 +372,44 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
         v[2 * j + 1] = x0 * sv[j] + x1 * cv[j];
       }
     }
+    // cross-entropy statistics: (max, sum of e^(y - max)) of each 64-column chunk, merged over
+    // the chunk's 8 threads, and y at the row's label (tile-local index selection)
+    if (e.xent_labels) {
+      constexpr float kLog2e = 1.4426950408889634f;
+      float m = -INFINITY, sx = 0.f;
+      if (ok) {
+        m = v[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) m = fmaxf(m, v[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sx += exp2f((v[i] - m) * kLog2e);
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const float mo = __shfl_xor(m, o, kWave), so = __shfl_xor(sx, o, kWave);
+        const float mn = fmaxf(m, mo);
+        sx = mn == -INFINITY ? 0.f : sx * exp2f((m - mn) * kLog2e) + so * exp2f((mo - mn) * kLog2e);
+        m = mn;
+      }
+      if (ok && (g & 7) == 0) {
+        float* st = e.xent_stats + (int64_t)t * e.xent_ld + 2 * (f / 64);
+        st[0] = m;
+        st[1] = sx;
+      }
+      if (ok) {
+        const int o = e.xent_labels[t] - f;
+        if (o >= 0 && o < 8) {
+          float val = v[0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) val = o == i ? v[i] : val;
+          e.xent_tgt[t] = val;
+        }
+      }
+    }
     const int fo = swiglu ? f / 2 : f;  // output column of v[0]
 
     if (mode == EPI_STORE) {
-      if (!ok) continue;
+      if (!ok || (!e.y && !e.n_split)) continue;  // no Y: the logits are not stored (XENT)
       if (swiglu) {
         store4(static_cast<char*>(e.y) + (int64_t)t * e.ldy * yb, e.y_dtype, fo, f32x4{v[0], v[1], v[2], v[3]});
       } else if (e.n_split) {

@@ -59,4 +59,13 @@ struct FinalizeArgs {
 };
 hipError_t launch_rmsnorm_finalize(const FinalizeArgs& a, hipStream_t stream);
 
+struct XentFinalizeArgs {
+  const float* stats;     // M x 2T (max, sum-exp) pairs, row stride ld
+  int64_t ld, M, T, n_cols;
+  const float* target;    // y at the label, per row
+  const int* labels;
+  float* loss;
+};
+hipError_t launch_xent_finalize(const XentFinalizeArgs& a, hipStream_t stream);
+
 }  // namespace fusedops

@@ -36,9 +36,11 @@
 extern "C" {
 #endif
 
-#define FUSEDOPS_ABI_VERSION 2
+#define FUSEDOPS_ABI_VERSION 3
 /* Width of one RMSNorm row partial: p[m,t] covers columns [128 t, 128 t + 128). */
 #define FUSEDOPS_PARTIAL_COLS 128
+/* Column width of the cross-entropy chunk statistics (XENT). */
+#define FUSEDOPS_XENT_COLS 64
 /* Largest LayerNorm row supported by fusedops_layernorm_gelu (elements). */
 #define FUSEDOPS_LN_MAX_COLS 16384
 
@@ -74,6 +76,7 @@ enum fusedops_dtype {
  *   h3 = r[m] * h2                      ROW_SCALE, or ROW_RMS (r from row partials)  [Epilogue] §模式A, Epilogue 2
  *   y  = act(h3)                        GELU_ERF | GELU_TANH | SWIGLU
  *   y  = rotate(y)                      ROPE: adjacent column pairs   [Epilogue] §背景, §模式B
+ *   XENT: per-row (max, sum-exp) of y over 64-column chunks + y at the label   [Epilogue] §模式C
  *   QUANT_FP8_ROW: Y is E4M3 codes with one fp32 scale per row    [Epilogue] §仿射量化与尾声的五步
  *   SPLIT_COLS: Y is written as n_split column blocks              [Fusion] §QKV投影融合
  *
@@ -109,6 +112,14 @@ enum fusedops_dtype {
  *                     formula of fusedops_rmsnorm_finalize, then used as ROW_SCALE's r: the light
  *                     reduction runs inside this GEMM, overlapping its mainloop ([Epilogue] §模式A,
  *                     Fig. 4). Not combinable with ROW_SCALE.
+ *   XENT              The stateful cross-entropy epilogue. in = labels (int32, length M; a label
+ *                     outside [0, N) marks an ignored row), out = stats (fp32, M x 2T with T =
+ *                     ceil(N / 64), row stride ld >= 2T): for chunk t of columns [64t, 64t + 64) the
+ *                     pair m = max y, s = sum e^(y - m) over the chunk's columns < N; out_v[0] =
+ *                     target (fp32, length M): y[m, label[m]] for rows with a valid label (others
+ *                     untouched). y is the fp32 value before any rounding. Y may be NULL (logits not
+ *                     stored). fusedops_cross_entropy_finalize merges the chunks. Not combinable with
+ *                     SWIGLU, QUANT_FP8_ROW or SPLIT_COLS.
  *   ROPE              in = table (fp32, M rows, row stride ld >= d floats), n_split = d (head width,
  *                     a multiple of 8). Column pair (2j, 2j+1) of output row m, with i = (2j mod d)/2,
  *                     becomes (a c - b s, a s + b c) where c = table[m][2i], s = table[m][2i+1]: row
@@ -131,7 +142,8 @@ enum fusedops_op_kind {
   FUSEDOPS_OP_DEQUANT_ROW = 11,
   FUSEDOPS_OP_DEQUANT_COL = 12,
   FUSEDOPS_OP_ROPE = 13,
-  FUSEDOPS_OP_ROW_RMS = 14
+  FUSEDOPS_OP_ROW_RMS = 14,
+  FUSEDOPS_OP_XENT = 15
 };
 
 enum fusedops_gelu_form {
@@ -167,7 +179,7 @@ typedef struct fusedops_op {
  *   ops    n_ops ops in canonical order (n_ops = 0 allowed; ops may be NULL then).
  *   Y      M x N_out (N_out = N/2 with SWIGLU, else N), row stride ldy, dtype out_dtype
  *          in {BF16, F16, F32}, or F8E4M3 exactly when QUANT_FP8_ROW is present.
- *          Must be NULL when SPLIT_COLS is present.
+ *          Must be NULL when SPLIT_COLS is present; may be NULL when XENT is present.
  *   workspace / workspace_bytes
  *          Device scratch of at least fusedops_linear_workspace_bytes(...) bytes, 16-byte
  *          aligned (0 bytes when no op needs one; then workspace may be NULL). Only
@@ -233,6 +245,23 @@ int32_t fusedops_rmsnorm_finalize(const float* partials, int64_t ldp, int64_t M,
                                   int64_t N, float eps, float* r, const void* h, int64_t ldh,
                                   const void* gamma, void* y, int64_t ldy, int32_t dtype,
                                   void* stream);
+
+/*
+ * fusedops_cross_entropy_finalize — the final merge of the XENT chunk statistics.
+ *
+ * Defines: [Epilogue] §模式C: per row, fold the chunks' (m, s) pairs along the vocabulary with
+ * m = max(m1, m2), s = s1 e^(m1 - m) + s2 e^(m2 - m) (a separate reduction, no atomics), then
+ * loss[i] = m + log s - target[i], the cross-entropy -y[i, label] + log sum_k e^y[i, k].
+ *
+ *   stats   fp32 M x 2T as XENT wrote it (T = ceil(n_cols / 64)), row stride ld >= 2T.
+ *   target  fp32 length M (XENT's out_v[0]); labels int32 length M; n_cols = N of that call.
+ *   loss    fp32 length M: the loss, or 0 for a row whose label is outside [0, n_cols).
+ * Errors: INVALID_ARG (null pointer, M < 1, n_cols < 1, ld < 2T), MISALIGNED (unaligned fp32 /
+ * int32 pointers), LAUNCH.
+ */
+int32_t fusedops_cross_entropy_finalize(const float* stats, int64_t ld, int64_t M, int64_t n_cols,
+                                        const float* target, const int32_t* labels, float* loss,
+                                        void* stream);
 
 /* The fixed partial width, FUSEDOPS_PARTIAL_COLS. */
 int32_t fusedops_partial_cols(void);

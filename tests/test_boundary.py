@@ -32,14 +32,14 @@ def test_header_symbols_are_exported():
 
 
 def test_constants():
-    assert B.abi_version() == 2
+    assert B.abi_version() == 3
     assert B.partial_cols() == 128
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
     assert B.status_string(0) == "ok"
     text = open(HEADER).read()
     assert "#define FUSEDOPS_PARTIAL_COLS 128" in text
-    assert "#define FUSEDOPS_ABI_VERSION 2" in text
+    assert "#define FUSEDOPS_ABI_VERSION 3" in text
 
 
 def lin(X=addr(0), ldx=64, W=addr(1), ldw=64, bias=None, M=32, N=64, K=64, in_dt=B.BF16, ops=(),
@@ -134,6 +134,29 @@ def test_row_rms_rules():
     assert lin(ops=[rms(inp=addr(7, 2))]) == B.ERR_MISALIGNED
     assert lin(ops=[rms(inp=addr(2))]) == B.ERR_INVALID_ARG             # partials overlap Y
     assert lin(ops=[mkop(B.OP_GELU_ERF, reserved=7)]) == B.ERR_INVALID_ARG  # reserved only for ROW_RMS
+
+
+def test_xent_rules():
+    def xe(labels=addr(7), stats=addr(8), target=addr(9), ld=2):
+        o = mkop(B.OP_XENT, dtype=B.F32, inp=labels, out=stats, ld=ld)
+        if target is not None:
+            o.out_v[0] = target
+        return o
+    # N = 64: one 64-column chunk, so ld >= 2
+    assert lin(ops=[xe(ld=1)]) == B.ERR_INVALID_ARG
+    assert lin(ops=[xe(labels=None)]) == B.ERR_INVALID_ARG
+    assert lin(ops=[xe(target=None)]) == B.ERR_INVALID_ARG
+    assert lin(ops=[mkop(B.OP_SWIGLU), xe()], ldy=32) == B.ERR_INVALID_ARG
+    assert lin(ops=[xe(stats=addr(2))]) == B.ERR_INVALID_ARG             # statistics overlap Y
+    assert lin(ops=[xe(target=addr(8, 4))]) == B.ERR_INVALID_ARG        # target overlaps statistics
+    assert lin(ops=[xe(labels=addr(7, 2))]) == B.ERR_MISALIGNED
+    assert lin(Y=None, ops=[]) == B.ERR_INVALID_ARG                     # Y may be NULL only with XENT
+    f = B.lib.fusedops_cross_entropy_finalize
+    assert f(None, 2, 4, 64, addr(1), addr(2), addr(3), None) == B.ERR_INVALID_ARG
+    assert f(addr(0), 1, 4, 64, addr(1), addr(2), addr(3), None) == B.ERR_INVALID_ARG   # ld < 2T
+    assert f(addr(0), 2, 0, 64, addr(1), addr(2), addr(3), None) == B.ERR_INVALID_ARG
+    assert f(addr(0), 2, 4, 64, addr(1), addr(2), addr(0), None) == B.ERR_INVALID_ARG   # loss overlaps stats
+    assert f(addr(0), 2, 4, 64, addr(1), addr(2), addr(3, 2), None) == B.ERR_MISALIGNED
 
 
 def test_op_list_rules():

@@ -511,3 +511,72 @@ def test_pattern_a_generic_chain_and_finalize_equivalence():
     assert st == B.OK
     torch.cuda.synchronize()
     np.testing.assert_allclose(host64(y2), host64(out["y"].view), rtol=2e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# cross-entropy epilogue (XENT) + final merge: chunk statistics, label gather, loss
+# ---------------------------------------------------------------------------
+
+def run_xent(M, N, K, *, store_logits=False, bias=False, act=None, in_dtype=I.BF16, seed=0):
+    rng = np.random.default_rng([303, M, N, K, seed])
+    if in_dtype == I.F8E4M3:
+        X, W = I.random_e4m3_codes(rng, (M, K)), I.random_e4m3_codes(rng, (N, K))
+        sa = (rng.uniform(0.5, 1.5, M) / 8.0).astype(np.float32)
+        sw = (rng.uniform(0.5, 1.5, N) / (8.0 * math.sqrt(K))).astype(np.float32)
+        xv, wv = O.e4m3_decode(X), O.e4m3_decode(W)
+    else:
+        X = I.random_stored(rng, (M, K), I.BF16, std=2.0)
+        W = I.random_stored(rng, (N, K), I.BF16, std=1 / math.sqrt(K))
+        sa = sw = None
+        xv, wv = I.to_f64(X, I.BF16), I.to_f64(W, I.BF16)
+    b = I.random_stored(rng, (N,), I.BF16, std=0.5) if bias else None
+    labels = rng.integers(0, N, size=M).astype(np.int32)
+    labels[::7] = -100                                   # ignored rows
+    labels[3::11] = N                                    # out of range: ignored too
+    note(f"xent M={M} N={N} K={K} logits={store_logits} bias={bias} act={act} in={in_dtype}")
+    T = -(-N // B.XENT_COLS)
+    stats = Guarded(M, 2 * T, I.F32, ld=2 * T + 2)
+    tgt = Guarded(1, M, I.F32)
+    y = Guarded(M, N, I.BF16) if store_logits else None
+    keep = {"lab": dev(labels, I.F32).view(torch.int32)}
+    ops = [B.op(ACT_OP[act])] if act else []
+    if sa is not None:
+        keep["sa"], keep["sw"] = dev(sa, I.F32), dev(sw, I.F32)
+        ops += [B.op(B.OP_DEQUANT_ROW, keep["sa"]), B.op(B.OP_DEQUANT_COL, keep["sw"])]
+    ops.append(B.xent_op(keep["lab"], stats.view, tgt.view[0]))
+    st = B.fusedops_linear_epilogue(dev(X, in_dtype), dev(W, in_dtype), y.view if y else None,
+                                    bias=dev(b, I.BF16) if bias else None, ops=ops, out_dtype=I.BF16)
+    assert st == B.OK, B.status_string(st)
+    loss = Guarded(1, M, I.F32)
+    st = B.fusedops_cross_entropy_finalize(stats.view, N, tgt.view[0], keep["lab"], loss.view[0])
+    assert st == B.OK, B.status_string(st)
+    torch.cuda.synchronize()
+    assert stats.intact() and tgt.intact() and loss.intact() and (y is None or y.intact())
+    ref = O.linear_epilogue(xv, wv, bias=None if b is None else I.to_f64(b, I.BF16), act=act,
+                            x_scale=None if sa is None else sa.astype(np.float64),
+                            w_scale=None if sw is None else sw.astype(np.float64))["y"]
+    m_ref, s_ref = O.xent_chunk_stats(ref, B.XENT_COLS)
+    got = host64(stats.view)
+    check = check_f32 if in_dtype != I.F8E4M3 else (lambda g, r, w: check_lowp(g, r, w))
+    check(got[:, 0::2], m_ref, "chunk max")
+    check(got[:, 1::2], s_ref, "chunk sum-exp")
+    valid = (labels >= 0) & (labels < N)
+    t_gpu = host64(tgt.view[0])
+    check(t_gpu[valid], ref[np.arange(M), np.clip(labels, 0, N - 1)][valid], "target logits")
+    sentinel = host64(Guarded(1, 1, I.F32).view[0])[0]
+    assert np.all(t_gpu[~valid] == sentinel), "target written for an ignored row"
+    l_ref = O.cross_entropy(ref, labels)
+    check(host64(loss.view[0]), l_ref, "loss")
+    if y is not None:
+        check_lowp(host64(y.view), ref, "logits")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 1000, 136), (17, 520, 40), (129, 4096, 64)])
+def test_xent_statistics_and_loss(M, N, K):
+    run_xent(M, N, K)
+
+
+def test_xent_with_logits_bias_activation_and_fp8_inputs():
+    run_xent(300, 1000, 136, store_logits=True, bias=True)
+    run_xent(70, 512, 64, act="gelu_tanh", seed=1)
+    run_xent(300, 520, 160, in_dtype=I.F8E4M3, seed=2)
