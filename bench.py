@@ -49,10 +49,12 @@ SUITE = [
     ("linear_gelu_f32_64x256x256", "latency"),
 ]
 DOMINANT = "mlp_up_gelu_bf16_8192x16384x4096"
-# Widening beyond the suite above (the pattern-A chain, RoPE, E4M3 inputs): timed and reported under "next_workloads",
+# Widening beyond the suite above (the pattern-A chain, the cross-entropy LM head, RoPE, E4M3
+# inputs): timed and reported under "next_workloads",
 # each against the fp8 MFMA peak, and not part of `value`.
 NEXT = [
     ("chain_outproj_gateup_rms_bf16_16384x2048x16384", "mfma"),
+    ("lmhead_xent_bf16_4096x32768x2048", "mfma"),
     ("qkv_bias_rope_split_bf16_4096x12288x4096", "mfma"),
     ("downproj_residual_fp8in_16384x2048x8192", "mfma"),
     ("mlp_up_gelu_fp8in_8192x16384x4096", "mfma"),

@@ -34,9 +34,10 @@ namespace epi {
 constexpr uint32_t kStatic = 1u << 31;
 constexpr uint32_t kBias = 1u << 0, kZ = 1u << 1, kAux = 1u << 2, kPart = 1u << 3, kGamma = 1u << 4,
                    kRscale = 1u << 5, kQuant = 1u << 6, kSplit = 1u << 7;
-// op lists with a RoPE rotation have no instance of their own (the generic one runs them)
+// op lists with a RoPE rotation have no instance of their own (the generic one runs them);
+// cross-entropy statistics (kXent) do
 constexpr uint32_t kRope = 1u << 20;
-constexpr uint32_t kXent = 1u << 21;  // so do op lists with cross-entropy statistics
+constexpr uint32_t kXent = 1u << 21;
 constexpr int kActShift = 8, kYShift = 10, kZShift = 12, kAuxShift = 14, kBiasShift = 16, kGammaShift = 18;
 
 constexpr uint32_t config(uint32_t ops, int act, int y_dtype, int z_dtype = FUSEDOPS_BF16,
@@ -76,6 +77,7 @@ struct Cfg {
   __device__ bool rscale() const { if constexpr (S) return F & kRscale; else return e.rscale || e.rms_p; }
   __device__ bool quant() const { if constexpr (S) return F & kQuant; else return e.quant != 0; }
   __device__ bool split() const { if constexpr (S) return F & kSplit; else return e.n_split != 0; }
+  __device__ bool xent() const { if constexpr (S) return F & kXent; else return e.xent_labels != nullptr; }
   __device__ int act() const { if constexpr (S) return (F >> kActShift) & 3; else return e.act; }
   __device__ int y_dt() const { if constexpr (S) return (F >> kYShift) & 3; else return e.y_dtype; }
   __device__ int z_dt() const { if constexpr (S) return (F >> kZShift) & 3; else return e.z_dtype; }
@@ -149,6 +151,7 @@ __device__ __forceinline__ f32x4 vec4(const void* p, int dt, int f, int N, float
 // values with `store` after issuing its own first loads, so the latency overlaps.
 struct VecPrefetch {
   float v[3];
+  int lab;
   template <uint32_t F>
   __device__ __forceinline__ void load(const EpiParams& e, int t0, int f0, int M, int N) {
     const epi::Cfg<F> cfg{e};
@@ -157,12 +160,15 @@ struct VecPrefetch {
     v[0] = cfg.bias() && f < N ? load1(e.bias, cfg.bias_dt(), f) : 0.f;
     v[1] = cfg.gamma() && f < N ? load1(e.gamma, cfg.gamma_dt(), f) : 1.f;
     v[2] = cfg.rscale() && t < M ? row_scale_of(e, t) : 0.f;
+    lab = cfg.xent() && t < M ? e.xent_labels[t] : -1;
   }
+  // svec: [0, 256) bias, [256, 512) column scale, [512, 768) row scale, [768, 1024) label bits
   __device__ __forceinline__ void store(float* svec) const {
     const int tid = threadIdx.x;
     svec[tid] = v[0];
     svec[256 + tid] = v[1];
     svec[512 + tid] = v[2];
+    svec[768 + tid] = __int_as_float(lab);
   }
 };
 
@@ -230,7 +236,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
 
   const int act = cfg.act();
   const bool pairs = act == ACT_SWIGLU;
-  const bool fused = !cfg.z() && !cfg.aux() && !cfg.part() && !cfg.quant();
+  const bool fused = !cfg.z() && !cfg.aux() && !cfg.part() && !cfg.quant() && !cfg.xent();
 
   // Stage the lane's values (4 per group, or the 2 SwiGLU outputs per group) in storage
   // type dt and store the tile to `d`. `val(fb, tb)` yields block (fb, tb); tiles larger
@@ -423,6 +429,67 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = post(acc[fb][tb], g, tb);
     }
+  }
+
+  if (cfg.xent()) {
+    // Cross-entropy statistics on the accumulators ([Epilogue] §模式C): a wave's 128 features
+    // are two 64-column chunks (block pairs fb 0-1 and 2-3); a lane holds 32 of a chunk's values
+    // for each of its tokens and lane l ^ 32 the other 32, so each (max, sum-exp) is an in-lane
+    // reduction plus one exchange. Columns at or past N are left out. The lane holding a token's
+    // label column writes the target.
+    constexpr float kLog2e = 1.4426950408889634f;
+    const int wbase = f0 + wf * 128;  // first column of the wave's 128
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int t = t0 + tk(tb);
+      const bool t_ok = t < M;
+      // the label's register in this lane, if the lane holds it: column wbase + 32 fb + 8 q +
+      // 4 hb + j sits in register 4 q + j of block fb
+      const int o = __float_as_int(svec[768 + tk(tb)]) - wbase;  // label, fetched before the mainloop
+      const bool mine = o >= 0 && o < 128 && wbase + o < N && ((o >> 2) & 1) == hb;
+      const int want = (o >> 5) * 16 + ((o >> 3) & 3) * 4 + (o & 3);  // fb * 16 + r
+      float tv = 0.f;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tv = want == fb * 16 + r ? acc[fb][tb][r] : tv;
+      if (mine) e.xent_tgt[t] = tv;
+      // columns at or past N (last tile only, a wave-uniform test) become -inf: they drop out
+      // of the maximum, and e^-inf = 0 out of the sum; they are never stored
+      if (wbase + 128 > N) {
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[fb][tb][r] = f0 + fl(fb, r >> 2) + (r & 3) < N ? acc[fb][tb][r] : -INFINITY;
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int cf = wbase + c * 64;  // first column of the chunk
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[2 * c + i][tb][r]);
+        float sx = 0.f;
+        const float mb = m == -INFINITY ? 0.f : m * kLog2e;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sx += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[2 * c + i][tb][r], kLog2e, -mb));
+        const float mo = __shfl_xor(m, 32, kWave), so = __shfl_xor(sx, 32, kWave);
+        const float mn = fmaxf(m, mo);
+        // (terms below 2^-126 of the chunk maximum flush to zero: the sums are at least 1)
+        sx = mn == -INFINITY ? 0.f
+                             : sx * __builtin_amdgcn_exp2f((m - mn) * kLog2e) + so * __builtin_amdgcn_exp2f((mo - mn) * kLog2e);
+        if (hb == 0 && t_ok && cf < N) {
+          float* st = e.xent_stats + (int64_t)t * e.xent_ld + 2 * (cf / 64);
+          st[0] = mn;
+          st[1] = sx;
+        }
+      }
+    }
+    if (!e.y) return;  // logits not stored
   }
 
   if (!cfg.quant()) {

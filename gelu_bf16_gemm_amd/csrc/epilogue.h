@@ -382,13 +382,14 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
 #pragma unroll
         for (int i = 1; i < 8; ++i) m = fmaxf(m, v[i]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sx += exp2f((v[i] - m) * kLog2e);
+        for (int i = 0; i < 8; ++i) sx += __builtin_amdgcn_exp2f((v[i] - m) * kLog2e);
       }
 #pragma unroll
       for (int o = 1; o < 8; o <<= 1) {
         const float mo = __shfl_xor(m, o, kWave), so = __shfl_xor(sx, o, kWave);
         const float mn = fmaxf(m, mo);
-        sx = mn == -INFINITY ? 0.f : sx * exp2f((m - mn) * kLog2e) + so * exp2f((mo - mn) * kLog2e);
+        sx = mn == -INFINITY ? 0.f
+                             : sx * __builtin_amdgcn_exp2f((m - mn) * kLog2e) + so * __builtin_amdgcn_exp2f((mo - mn) * kLog2e);
         m = mn;
       }
       if (ok && (g & 7) == 0) {

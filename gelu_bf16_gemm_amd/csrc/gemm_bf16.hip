@@ -38,7 +38,7 @@ constexpr int kTileBytes = 256 * BK * 2;  // one operand tile in LDS (32 KB)
 template <uint32_t F>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];  // [stage][W, X]
-  __shared__ __attribute__((aligned(16))) float svec[3 * 256];               // epilogue vectors
+  __shared__ __attribute__((aligned(16))) float svec[4 * 256];               // epilogue vectors
   __shared__ int slot[2];
 
   const int tid = threadIdx.x;
@@ -237,8 +237,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
 }
 
 // Epilogue configurations with an instance of their own (the op sets of the fused QKV
-// projection, MLP-up, out-projection, gate/up, FP8 gate/up, and gate/up after a deferred
-// RMSNorm); any other op list runs the generic instance, which reads its choices at run time.
+// projection, MLP-up, out-projection, gate/up, FP8 gate/up, gate/up after a deferred RMSNorm,
+// and the LM head with cross-entropy statistics); any other op list runs the generic instance,
+// which reads its choices at run time.
 constexpr uint32_t kCfgBiasGeluErf = epi::config(epi::kBias, ACT_GELU_ERF, FUSEDOPS_BF16);
 constexpr uint32_t kCfgBiasSplit = epi::config(epi::kBias | epi::kSplit, ACT_NONE, FUSEDOPS_BF16);
 constexpr uint32_t kCfgResidualRms = epi::config(epi::kZ | epi::kAux | epi::kPart | epi::kGamma, ACT_NONE,
@@ -246,6 +247,7 @@ constexpr uint32_t kCfgResidualRms = epi::config(epi::kZ | epi::kAux | epi::kPar
 constexpr uint32_t kCfgSwiglu = epi::config(0, ACT_SWIGLU, FUSEDOPS_BF16);
 constexpr uint32_t kCfgSwigluFp8 = epi::config(epi::kQuant, ACT_SWIGLU, FUSEDOPS_F8E4M3);
 constexpr uint32_t kCfgRscaleSwiglu = epi::config(epi::kRscale, ACT_SWIGLU, FUSEDOPS_BF16);
+constexpr uint32_t kCfgXent = epi::config(epi::kXent, ACT_NONE, FUSEDOPS_BF16);
 
 const void* t256_kernel_for(const EpiParams& e) {
   switch (epi::config_of(e)) {
@@ -255,6 +257,7 @@ const void* t256_kernel_for(const EpiParams& e) {
     case kCfgSwiglu: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgSwiglu>);
     case kCfgSwigluFp8: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgSwigluFp8>);
     case kCfgRscaleSwiglu: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgRscaleSwiglu>);
+    case kCfgXent: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgXent>);
     default: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<0>);
   }
 }

@@ -48,7 +48,7 @@ __device__ __forceinline__ f32x16 mfma_e4m3(const i32x8& a, const i32x8& b, cons
 template <uint32_t F>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_t256_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];  // [stage][W, X]
-  __shared__ __attribute__((aligned(16))) float svec[3 * 256];               // epilogue vectors
+  __shared__ __attribute__((aligned(16))) float svec[4 * 256];               // epilogue vectors
   __shared__ __attribute__((aligned(16))) float dqv[2 * 256];                // sw[f], sa[t]
   __shared__ int slot[2];
 

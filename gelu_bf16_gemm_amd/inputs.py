@@ -118,6 +118,10 @@ WORKLOADS = {
     # computed from the partials (ROW_RMS) before SwiGLU.
     "chain_outproj_gateup_rms_bf16_16384x2048x16384": dict(config_id=13, kind="chain", M=16384, d=2048,
                                                            K0=2048, N2=16384, eps=1e-6, act="swiglu"),
+    # LM head with the cross-entropy epilogue (32K vocabulary, hidden 2048); logits not stored.
+    "lmhead_xent_bf16_4096x32768x2048": dict(config_id=14, kind="linear", M=4096, N=32768, K=2048,
+                                             in_dtype=BF16, bias=False, act=None, xent=True,
+                                             out_dtype=BF16),
     # The fused QKV projection with RoPE on its Q and K blocks (head width 128).
     "qkv_bias_rope_split_bf16_4096x12288x4096": dict(config_id=12, kind="linear", M=4096, N=12288,
                                                      K=4096, in_dtype=BF16, bias=True, act=None,
@@ -134,7 +138,7 @@ WORKLOADS = {
 }
 
 # tensor ids inside one config
-_T_X, _T_W, _T_B, _T_Z, _T_GAMMA, _T_BETA, _T_SA, _T_SW, _T_ROPE, _T_W1 = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9
+_T_X, _T_W, _T_B, _T_Z, _T_GAMMA, _T_BETA, _T_SA, _T_SW, _T_ROPE, _T_W1, _T_LAB = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
 
 
 def random_e4m3_codes(rng: np.random.Generator, shape, e_lo: int = 4, e_hi: int = 10) -> np.ndarray:
@@ -176,6 +180,8 @@ def make_linear_inputs(spec: dict, seed: int = 0, M: int | None = None, N: int |
         out["z"] = store(normal(rng_for(cid, _T_Z, seed), (M, N)), vec_dt)
     if spec.get("col_scale"):
         out["gamma"] = store(normal(rng_for(cid, _T_GAMMA, seed), (N,), mean=1.0, std=0.1), vec_dt)
+    if spec.get("xent"):
+        out["labels"] = rng_for(cid, _T_LAB, seed).integers(0, N, size=M).astype(np.int32)
     if spec.get("rope"):
         # per-row cos / sin of uniformly drawn angles (a rotation table; no frequency schedule)
         d = spec["rope"]

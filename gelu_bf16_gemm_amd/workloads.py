@@ -61,7 +61,14 @@ class LinearRun:
         self.scales = torch.empty(M, dtype=torch.float32, device=dev) if quant else None
         self.split = None
         self.y = None
-        if spec.get("split"):
+        self.xent = None
+        if spec.get("xent"):
+            T = -(-N // B.XENT_COLS)
+            self.xent = {"labels": torch.from_numpy(inp["labels"]).cuda(),
+                         "stats": torch.empty((M, 2 * T), dtype=torch.float32, device=dev),
+                         "target": torch.empty(M, dtype=torch.float32, device=dev),
+                         "loss": torch.empty(M, dtype=torch.float32, device=dev)}
+        elif spec.get("split"):
             d = N // spec["split"]
             self.split = [torch.empty((M, d), dtype=_TORCH[self.out_dtype], device=dev) for _ in range(spec["split"])]
         else:
@@ -101,6 +108,9 @@ class LinearRun:
             ops.append(B.op(B.OP_DEQUANT_COL, self.sw))
         if self.rope_cs is not None:
             ops.append(B.op(B.OP_ROPE, self.rope_cs, head_dim=s["rope"]))
+        if self.xent is not None:
+            x = self.xent
+            ops.append(B.xent_op(x["labels"], x["stats"], x["target"]))
         return ops
 
     def launch(self, i: int = 0, stream=None) -> None:
@@ -110,6 +120,10 @@ class LinearRun:
                                            workspace=self.ws, out_dtype=self.out_dtype, stream=stream))
         if self.partials is not None:
             B.check(B.fusedops_rmsnorm_finalize(self.partials, self.N, self.eps, self.r, stream=stream))
+        if self.xent is not None:
+            x = self.xent
+            B.check(B.fusedops_cross_entropy_finalize(x["stats"], self.N, x["target"], x["labels"], x["loss"],
+                                                      stream=stream))
 
     def outputs(self, rows) -> dict:
         idx = torch.as_tensor(np.asarray(rows), device="cuda")
@@ -125,6 +139,9 @@ class LinearRun:
             out["r"] = _host64(self.r.index_select(0, idx))
         if self.scales is not None:
             out["scales"] = _host64(self.scales.index_select(0, idx))
+        if self.xent is not None:
+            for k in ("stats", "target", "loss"):
+                out[k] = _host64(self.xent[k].index_select(0, idx))
         return out
 
     def workspace_ok(self) -> bool:
@@ -152,6 +169,11 @@ class LinearRun:
             b += N * 4
         if self.rope_cs is not None:
             b += self.rope_cs.numel() * 4
+        if self.xent is not None:
+            # labels, statistics written and read back, target, loss; no logits when y is absent
+            b += M * 4 + self.xent["stats"].numel() * 4 * 2 + M * 4 * 2 + M * 4
+            if self.y is None:
+                b -= M * self.n_out * es_out
         if self.z is not None:
             b += M * N * 2
         if self.aux is not None:

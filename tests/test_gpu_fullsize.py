@@ -59,6 +59,13 @@ def test_linear_workload_full_size(name):
         s_ref = O.fp8_row_scale(np.abs(ref["y"]).max(axis=1)).astype(np.float64)
         np.testing.assert_allclose(s.astype(np.float64), s_ref, rtol=2e-4)
         assert run.workspace_ok()
+    elif spec.get("xent"):
+        lab = inp["labels"][rows]
+        m_ref, s_ref = O.xent_chunk_stats(ref["y"], 64)
+        check_f32(out["stats"][:, 0::2], m_ref, f"{name} chunk max")
+        check_f32(out["stats"][:, 1::2], s_ref, f"{name} chunk sum-exp")
+        check_f32(out["target"], ref["y"][np.arange(len(rows)), lab], f"{name} target")
+        check_f32(out["loss"], O.cross_entropy(ref["y"], lab), f"{name} loss")
     elif spec.get("split"):
         d = spec["N"] // spec["split"]
         for i, blk in enumerate(out["split"]):
