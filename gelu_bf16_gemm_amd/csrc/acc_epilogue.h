@@ -190,6 +190,24 @@ __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int r
   const int cshift = __builtin_ctz(C);
   const int per = 16 / d.es;  // elements per chunk
   const int sw = (int)d.split_w;
+  // Interior tile (the usual case): every row valid and the whole column range inside the
+  // output and inside one destination. Thread tid then copies chunk tid % C of rows
+  // tid / C, tid / C + 256 / C, ... with no per-chunk tests (C <= 64, so every thread has
+  // a chunk); a wave stores 1 KB of consecutive row pieces per instruction.
+  const int col_end = d.col0 + C * per;
+  const int seg0 = sw ? d.col0 / sw : 0;
+  if (row0 + R <= M && col_end <= d.cols && (!sw || (col_end - 1) / sw == seg0)) {
+    const int c = threadIdx.x & (C - 1);
+    const int rstep = kEpiThreads >> cshift;
+    const int m = (C < 32 ? C : 32) - 1;
+    int r = threadIdx.x >> cshift;
+    uint8_t* g = d.at(seg0) + ((int64_t)(row0 + r) * d.ld + (d.col0 - seg0 * sw) + c * per) * d.es;
+    const int64_t gstep = (int64_t)rstep * d.ld * d.es;
+#pragma unroll 8
+    for (; r < R; r += rstep, g += gstep)
+      *reinterpret_cast<u32x4*>(g) = *reinterpret_cast<const u32x4*>(lds + r * C * 16 + ((c ^ (r & m)) << 4));
+    return;
+  }
 #pragma unroll 8
   for (int id = threadIdx.x; id < R * C; id += kEpiThreads) {
     const int r = id >> cshift, c = id & (C - 1);

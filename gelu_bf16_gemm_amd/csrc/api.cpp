@@ -363,7 +363,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
     const int tile_f = kern == Kernel::T256 ? gemm_bf16_t256_tile_f()
                        : kern == Kernel::FP8 ? gemm_fp8_t256_tile_f()
                        : kern == Kernel::SKINNY ? gemm_bf16_skinny_tile_f() : gemm_f32_tile_f();
-    const void* sym = kern == Kernel::T256 ? gemm_bf16_t256_symbol(a.ep)
+    const void* sym = kern == Kernel::T256 ? gemm_bf16_t256_symbol(a)
                       : kern == Kernel::FP8 ? gemm_fp8_t256_symbol(a.ep)
                       : kern == Kernel::SKINNY ? gemm_bf16_skinny_symbol() : gemm_f32_symbol();
     const int threads = kern == Kernel::SKINNY ? gemm_bf16_skinny_threads() : 256;

@@ -3,15 +3,19 @@
 // Mainloop ([Fusion] §Linear算子剖析; [Epilogue] §主循环与尾声): one workgroup of
 // 4 waves owns a 256-feature x 256-token output tile and walks K in steps of 64.
 // Each step's W and X tiles (256 rows x 64 bf16, both K-contiguous in HBM) are
-// staged in LDS, double buffered, with two register stage sets in front: during
-// step s the MFMAs read LDS buffer s&1 while the data of step s+1 (already in
-// registers) is written to the other buffer and the 16-byte global loads of step
-// s+2 are issued; MFMAs, operand reads, fills and loads are interleaved so that
-// the single wave per SIMD always has matrix work queued. One barrier per step.
+// staged in LDS, double buffered. Two ways of filling LDS:
+//  * LDS DMA (tiles with whole W rows and an even number of K steps, every workload
+//    shape): buffer loads write LDS directly, two steps ahead, into space the MFMAs of
+//    the current step have just finished reading (mainloop_dma);
+//  * register staging (any shape): during step s the MFMAs read LDS buffer s&1 while
+//    the data of step s+1 (already in registers) is written to the other buffer and the
+//    16-byte global loads of step s+2 are issued. One barrier per step.
+// In both, MFMAs, operand reads and fills or loads are interleaved so that the single
+// wave per SIMD always has matrix work queued.
 //
 // LDS layout: a 64-wide K tile row is 128 bytes = 8 chunks of 16 bytes, XOR-swizzled
-// per row (see swz) so the ds_read_b128 operand fetches and the ds_write_b128
-// fills are free of bank conflicts.
+// per row (see swz) so the ds_read_b128 operand fetches and the fills are free of
+// bank conflicts.
 //
 // Each wave computes 128 features x 128 tokens as 4 x 4 v_mfma_f32_32x32x16_bf16
 // blocks (A = W rows, B = X rows, D[f][t]); the epilogue then stages the tile in LDS.
@@ -35,7 +39,194 @@ constexpr int BK = 64;    // K per step
 constexpr int kThreads = 256;
 constexpr int kTileBytes = 256 * BK * 2;  // one operand tile in LDS (32 KB)
 
+// One 16-byte-per-lane LDS DMA: lane l's 16 bytes at rsrc + soff + voff land at LDS byte
+// lds + 16 l. Issued as inline assembly so that the compiler, which cannot tell the DMA's LDS
+// destination from the buffers being read, does not wait for it before every LDS read; M0
+// (the LDS base of the DMA) is set inside the same statement. Every wait on these DMAs is
+// placed by hand (dma_wait_barrier).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "s"(lds)
+               : "memory");
+}
+
+// Wait until at most N of this wave's LDS DMAs are still in flight and all of its LDS reads
+// have returned, then meet the other waves. The DMAs write LDS without the compiler tracking
+// them, so every wait on them is placed by hand; the "memory" clobber keeps the compiler from
+// moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void dma_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Mainloop fed by LDS DMA (buffer loads that write LDS directly: no staging registers and no
+// ds_write), for tiles whose W rows and K steps are all whole (N % 256 == 0, K % 128 == 0;
+// checked on the host). Out-of-range lanes of an LDS DMA leave LDS untouched instead of
+// writing zeros, so X rows past M are read from the tile's last valid row instead (their
+// outputs are never stored and no reduction mixes rows).
+//
+// Buffers: W and X tiles of a step (256 rows x 128 bytes each, the swizzled layout of
+// tile256.h), two of each. A step is walked in two regions: A multiplies feature blocks 0-1
+// (W rows wf*128 + 0..63 of each wave's half), B blocks 2-3, each wave against its 128 tokens,
+// whose fragments for the whole step sit in registers (read in region A of the previous step).
+// A region reads the W fragments the next region multiplies, so W blocks 2-3 of a buffer are
+// free after A and blocks 0-1 after B, and X is free once its fragments are in registers.
+// Each region ends with a barrier after which the space just freed is refilled by DMA with
+// data two steps ahead. Per wave and step the DMAs are (2 instructions per W block, 8 for X)
+//   region A: W blocks 0-1 of s+2        region B: W blocks 2-3 of s+2, X of s+3
+// so every DMA has 1.5 steps to land, and each is paired with an MFMA: the four waves leave a
+// barrier together, and DMAs issued back to back would queue at the CU's address unit while
+// the matrix core idles. Each barrier waits for exactly the DMAs the next region reads; the
+// counts follow from this fixed issue order, which the prologue reproduces.
 template <uint32_t F>
+__device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, float* svec,
+                                             const accepi::VecPrefetch& vp, f32x16 (&acc)[4][4], int t0, int f0) {
+  constexpr int kBuf = 2 * kTileBytes;  // one stage: W tile then X tile
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wf = wave >> 1, wt = wave & 1;
+  const int K = a.K;
+  const int steps = K / BK;
+  const int x_rows = min(BT, a.M - t0);
+  const uint16_t* Wt = static_cast<const uint16_t*>(a.W) + (int64_t)f0 * a.ldw;
+  const uint16_t* Xt = static_cast<const uint16_t*>(a.X) + (int64_t)t0 * a.ldx;
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wt, (uint32_t)(((int64_t)(BF - 1) * a.ldw + K) * 2));
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xt, (uint32_t)(((int64_t)(x_rows - 1) * a.ldx + K) * 2));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;  // LDS byte address of smem
+
+  // One DMA instruction fills 8 consecutive LDS rows (1 KB): lane l writes position l % 8 of
+  // row l / 8, which holds logical chunk (l % 8) ^ swz(row). For a group of rows starting at a
+  // multiple of 8, swz(row) = l / 8 ^ (bit 3 of the group's first row).
+  const int l8 = lane >> 3, p8 = lane & 7;
+  // W: wave w fills rows (w >> 1) * 128 + j * 32 + (w & 1) * 16 + g * 8 .. of block j, g = 0, 1
+  const int w_row0 = (wave >> 1) * 128 + (wave & 1) * 16;
+  uint32_t w_lane[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) w_lane[g] = (uint32_t)(l8 * a.ldw * 2 + ((p8 ^ l8 ^ g) << 4));
+  // X: wave w fills rows w * 64 + g * 8 .., g = 0..7 (rows past M read row M - 1)
+  uint32_t x_lane[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const int r = min(wave * 64 + g * 8 + l8, x_rows - 1);
+    x_lane[g] = (uint32_t)(r * a.ldx * 2 + ((p8 ^ l8 ^ (g & 1)) << 4));
+  }
+  // DMAs of steps past the last read nothing (the offset's top bit puts them out of range)
+  // and leave LDS as it is; they are still issued so that the wait counts stay exact.
+  auto dma_w1 = [&](int t, int j, int g) __attribute__((always_inline)) {
+    const uint32_t oob = t < steps ? 0u : kOobOffset;
+    const int r0 = w_row0 + j * 32 + g * 8;
+    lds_dma16(rW, w_lane[g] | oob, (uint32_t)(r0 * a.ldw * 2 + t * BK * 2), lds0 + (t & 1) * kBuf + r0 * 128);
+  };
+  auto dma_x1 = [&](int t, int g) __attribute__((always_inline)) {
+    const uint32_t oob = t < steps ? 0u : kOobOffset;
+    lds_dma16(rX, x_lane[g] | oob, (uint32_t)(t * BK * 2),
+              lds0 + (t & 1) * kBuf + kTileBytes + (wave * 64 + g * 8) * 128);
+  };
+  auto dma_w = [&](int t, int j) __attribute__((always_inline)) { dma_w1(t, j, 0); dma_w1(t, j, 1); };
+  auto dma_x = [&](int t, int half) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) dma_x1(t, half * 4 + g);
+  };
+
+  // Operand fragments: row (lane % 32) of a 32-row block, logical chunk 2 kk + lane / 32.
+  const int a_row0 = wf * 128 + (lane & 31);
+  const int b_row0 = wt * 128 + (lane & 31);
+  uint32_t koff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = (uint32_t)((((kk * 2 + (lane >> 5)) ^ swz(lane & 31))) << 4);
+  bf16x8 wfr[2][2][4];  // W fragments of two feature blocks [set][block][kk], double buffered
+  bf16x8 xf[2][4][4];   // X fragments of a whole step [set][token block][kk], double buffered
+  auto frag = [&](int t, bool x, int row, int kk) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(smem + (t & 1) * kBuf + (x ? kTileBytes : 0) + row * 128 + koff[kk]);
+  };
+
+  // One half-step region: MFMA i of the 32 (feature block J0 + i / 16, kk = i / 4 % 4, token
+  // block i % 4), read i of the region after MFMA i (reads first), DMAs at the positions
+  // below; sched barriers keep that order. rd(i) and dm(d) are the region's reads and DMAs.
+  auto region = [&](auto j0_c, auto nr_c, auto nd_c, const bf16x8 (&w)[2][4], const bf16x8 (&x)[4][4], auto&& rd,
+                    auto&& dm) __attribute__((always_inline)) {
+    constexpr int J0 = decltype(j0_c)::value, NR = decltype(nr_c)::value, ND = decltype(nd_c)::value;
+    static_for<0, 32>([&](auto i_c) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_c)::value;
+      constexpr int jb = i / 16, kk = (i / 4) % 4, tb = i % 4;
+      __builtin_amdgcn_sched_barrier(0);
+      acc[J0 + jb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[jb][kk], x[tb][kk], acc[J0 + jb][tb], 0, 0, 0);
+      if constexpr (i < NR) rd(i_c);
+      // DMAs at positions 3, 11, 19, 27 (four) or at the odd positions 1, 3, .. (more)
+      constexpr int d = ND == 4 ? ((i % 8) == 3 ? i / 8 : -1) : ((i & 1) && i / 2 < ND ? i / 2 : -1);
+      if constexpr (d >= 0) dm(std::integral_constant<int, d>{});
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using C4 = std::integral_constant<int, 4>;
+  using C8 = std::integral_constant<int, 8>;
+  using C12 = std::integral_constant<int, 12>;
+  using C24 = std::integral_constant<int, 24>;
+
+  // Step s with X fragments in set P (the next step's go to set P ^ 1). Region A multiplies
+  // feature blocks 0-1 (W fragments in wfr[0]) and reads blocks 2-3 and all of X of s+1;
+  // region B multiplies blocks 2-3 and reads blocks 0-1 of s+1.
+  auto step = [&](auto p_c, int s) __attribute__((always_inline)) {
+    constexpr int P = decltype(p_c)::value;
+    // A: DMA W blocks 0-1 of s+2 (their space was read in B of s-1)
+    region(std::integral_constant<int, 0>{}, C24{}, C4{}, wfr[0], xf[P],
+           [&](auto r) __attribute__((always_inline)) {
+             constexpr int q = decltype(r)::value;
+             if constexpr (q < 8) wfr[1][q / 4][q % 4] = frag(s, false, a_row0 + (2 + q / 4) * 32, q % 4);
+             else xf[P ^ 1][(q - 8) / 4][(q - 8) % 4] = frag(s + 1, true, b_row0 + ((q - 8) / 4) * 32, (q - 8) % 4);
+           },
+           [&](auto d) __attribute__((always_inline)) { dma_w1(s + 2, decltype(d)::value / 2, decltype(d)::value % 2); });
+    dma_wait_barrier<16>();  // next: W blocks 0-1 of s+1 (region A of s-1)
+    // B: DMA W blocks 2-3 of s+2 and X of s+3 (their space was read in A of s)
+    region(std::integral_constant<int, 2>{}, C8{}, C12{}, wfr[1], xf[P],
+           [&](auto r) __attribute__((always_inline)) {
+             constexpr int q = decltype(r)::value;
+             wfr[0][q / 4][q % 4] = frag(s + 1, false, a_row0 + (q / 4) * 32, q % 4);
+           },
+           [&](auto d) __attribute__((always_inline)) {
+             constexpr int q = decltype(d)::value;
+             if constexpr (q < 4) dma_w1(s + 2, 2 + q / 2, q % 2);
+             else dma_x1(s + 3, q - 4);
+           });
+    dma_wait_barrier<16>();  // next: W blocks 2-3 of s+1 and X of s+2 (region B of s-1)
+  };
+
+  // Prologue: the DMAs of steps 0 and 1 in the loop's own order (X of step 0 first), the
+  // fragments of step 0, then the rest of that order up to the end of step -1.
+  dma_x(0, 0); dma_x(0, 1);
+  dma_w(0, 0); dma_w(0, 1); dma_w(0, 2); dma_w(0, 3); dma_x(1, 0); dma_x(1, 1);
+  dma_w(1, 0); dma_w(1, 1);
+  if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
+  dma_wait_barrier<16>();  // X and W blocks 0-1 of step 0
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) xf[0][tb][kk] = frag(0, true, b_row0 + tb * 32, kk);
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) wfr[0][jb][kk] = frag(0, false, a_row0 + jb * 32, kk);
+  dma_wait_barrier<40>();  // every wave holds its step-0 fragments: X buffer 0 and W blocks 0-1 are free
+  dma_w(1, 2); dma_w(1, 3); dma_x(2, 0); dma_x(2, 1);
+  dma_wait_barrier<16>();  // W blocks 2-3 of step 0 and X of step 1
+
+#pragma clang loop unroll(disable)
+  for (int s = 0; s < steps; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+  }
+  dma_wait_barrier<0>();  // every DMA has landed and every fragment read is done before LDS is reused
+}
+
+template <uint32_t F, bool kDma>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];  // [stage][W, X]
   __shared__ __attribute__((aligned(16))) float svec[4 * 256];               // epilogue vectors
@@ -63,157 +254,162 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   accepi::VecPrefetch vp;
   if constexpr ((F & epi::kStatic) != 0) vp.load<F>(a.ep, t0, f0, a.M, a.N);
 
-  // Buffer resources over this tile's rows: rows past M / N read as zero.
-  const int w_rows = min(BF, a.N - f0), x_rows = min(BT, a.M - t0);
-  const uint16_t* Wt = static_cast<const uint16_t*>(a.W) + (int64_t)f0 * a.ldw;
-  const uint16_t* Xt = static_cast<const uint16_t*>(a.X) + (int64_t)t0 * a.ldx;
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wt, (uint32_t)(((int64_t)(w_rows - 1) * a.ldw + K) * 2));
-  const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xt, (uint32_t)(((int64_t)(x_rows - 1) * a.ldx + K) * 2));
-
-  // Global->LDS assignment: 8 chunks per thread per operand; chunk id j*256 + tid is
-  // row j*32 + tid/8, 16-byte chunk tid%8 (8 threads read one 128-byte row segment).
-  // The per-lane part of the address is a VGPR; the j*32-row part is a scalar offset.
-  const int ld_row = tid >> 3, ld_c = tid & 7;
-  const uint32_t w_voff = (uint32_t)(ld_row * a.ldw * 2 + ld_c * 16);
-  const uint32_t x_voff = (uint32_t)(ld_row * a.ldx * 2 + ld_c * 16);
-  const uint32_t w_rowstep = (uint32_t)(32 * a.ldw * 2), x_rowstep = (uint32_t)(32 * a.ldx * 2);
-  // rows j*32 + ld_row share row & 15, so the fill offset of chunk j is st_off + j * 4096
-  const uint32_t st_off = lds_off(ld_row, ld_c);
-
-  // One register stage set: chunks 0..7 of W then 0..7 of X. During step s, quarter q of
-  // the set (holding step s+1) is written to LDS buffer (s+1)&1, then the same registers
-  // receive quarter q of step s+2 — a full step of latency for every load.
-  u32x4 stage[16];
-
-  // Chunks at or past K read as zero: the high offset bit makes the access out of range
-  // (arithmetic rather than a select, so the loads stay branch-free).
-  auto load_q = [&](int k0, int q) __attribute__((always_inline)) {
-    const uint32_t oob = (uint32_t)(k0 + ld_c * 8 >= K) << 31;  // K is a multiple of 8
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = q * 4 + i;
-      const int j = c & 7;
-      const uint32_t voff = ((c < 8 ? w_voff : x_voff) + (uint32_t)k0 * 2) | oob;
-      stage[c] = __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? rW : rX, voff,
-                                                       j * (c < 8 ? w_rowstep : x_rowstep), 0);
-    }
-  };
-  auto store_q = [&](int buf, int q) __attribute__((always_inline)) {
-    uint8_t* wb = smem + buf * (2 * kTileBytes) + st_off;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = q * 4 + i;
-      *reinterpret_cast<u32x4*>(wb + (c < 8 ? 0 : kTileBytes) + (c & 7) * 4096) = stage[c];
-    }
-  };
-
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  // Per-lane operand read offsets: row (lane % 32) of each 32-row block, logical chunk
-  // 2*kk + lane/32. Block bases are multiples of 32 rows, so the swizzle uses lane % 32.
-  const int a_row0 = wf * 128 + (lane & 31);
-  const int b_row0 = wt * 128 + (lane & 31);
-  uint32_t koff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) koff[kk] = (uint32_t)((((kk * 2 + (lane >> 5)) ^ swz(lane & 31))) << 4);
+  if constexpr (kDma) {
+    mainloop_dma<F>(a, smem, svec, vp, acc, t0, f0);
+  } else {
+    // Buffer resources over this tile's rows: rows past M / N read as zero.
+    const int w_rows = min(BF, a.N - f0), x_rows = min(BT, a.M - t0);
+    const uint16_t* Wt = static_cast<const uint16_t*>(a.W) + (int64_t)f0 * a.ldw;
+    const uint16_t* Xt = static_cast<const uint16_t*>(a.X) + (int64_t)t0 * a.ldx;
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wt, (uint32_t)(((int64_t)(w_rows - 1) * a.ldw + K) * 2));
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xt, (uint32_t)(((int64_t)(x_rows - 1) * a.ldx + K) * 2));
 
-  bf16x8 fa[2][4], fb_[2][4];
-  auto read_frags = [&](int buf, int kk, bf16x8 (&af)[4], bf16x8 (&bf)[4]) __attribute__((always_inline)) {
-    const uint8_t* wb = smem + buf * (2 * kTileBytes);
-    const uint8_t* xb = wb + kTileBytes;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) af[f] = *reinterpret_cast<const bf16x8*>(wb + (a_row0 + f * 32) * 128 + koff[kk]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) bf[t] = *reinterpret_cast<const bf16x8*>(xb + (b_row0 + t * 32) * 128 + koff[kk]);
-  };
+    // Global->LDS assignment: 8 chunks per thread per operand; chunk id j*256 + tid is
+    // row j*32 + tid/8, 16-byte chunk tid%8 (8 threads read one 128-byte row segment).
+    // The per-lane part of the address is a VGPR; the j*32-row part is a scalar offset.
+    const int ld_row = tid >> 3, ld_c = tid & 7;
+    const uint32_t w_voff = (uint32_t)(ld_row * a.ldw * 2 + ld_c * 16);
+    const uint32_t x_voff = (uint32_t)(ld_row * a.ldx * 2 + ld_c * 16);
+    const uint32_t w_rowstep = (uint32_t)(32 * a.ldw * 2), x_rowstep = (uint32_t)(32 * a.ldx * 2);
+    // rows j*32 + ld_row share row & 15, so the fill offset of chunk j is st_off + j * 4096
+    const uint32_t st_off = lds_off(ld_row, ld_c);
 
-  // One K step s from LDS buffer s&1: the MFMAs of the step, the fill of buffer (s+1)&1
-  // from the stage set (data of step s+1), and the loads of step s+2 into the stage set.
-  // The fills and loads are done in sub-steps 0..2 and the step's one barrier comes after
-  // sub-step 2: by then every wave has read its last fragments of buffer s&1 and written its
-  // part of buffer (s+1)&1. Sub-step 3's MFMAs then run while the first fragments of step
-  // s+1 are read, so no fragment read waits behind the barrier. The fragments of sub-step 0
-  // arrive from the previous step (or the prologue). The last two steps fill and load past
-  // the end of K: those loads read zeros into a buffer that is not read again.
-  auto kstep = [&](int s) __attribute__((always_inline)) {
-    const int CUR = s & 1;
-    // sub-step kk is a compile-time constant so every register array index is static
-    auto sub = [&](auto kk_c) __attribute__((always_inline)) {
-      constexpr int kk = decltype(kk_c)::value;
-      // keep each sub-step's work together: at most one sub-step of fragments in flight
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kk < 3) read_frags(CUR, kk + 1, fa[(kk + 1) & 1], fb_[(kk + 1) & 1]);
-      else read_frags(CUR ^ 1, 0, fa[0], fb_[0]);
+    // One register stage set: chunks 0..7 of W then 0..7 of X. During step s, quarter q of
+    // the set (holding step s+1) is written to LDS buffer (s+1)&1, then the same registers
+    // receive quarter q of step s+2 — a full step of latency for every load.
+    u32x4 stage[16];
+
+    // Chunks at or past K read as zero: the high offset bit makes the access out of range
+    // (arithmetic rather than a select, so the loads stay branch-free).
+    auto load_q = [&](int k0, int q) __attribute__((always_inline)) {
+      const uint32_t oob = (uint32_t)(k0 + ld_c * 8 >= K) << 31;  // K is a multiple of 8
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][f], fb_[kk & 1][t], acc[f][t], 0, 0, 0);
-      // fills and loads: quarters 0 and 1 in sub-step 0, 2 in sub-step 1, 3 in sub-step 2
-      if constexpr (kk == 0) {
-        store_q(CUR ^ 1, 0);
-        store_q(CUR ^ 1, 1);
-        load_q((s + 2) * BK, 0);
-        load_q((s + 2) * BK, 1);
-      } else if constexpr (kk < 3) {
-        store_q(CUR ^ 1, kk + 1);
-        load_q((s + 2) * BK, kk + 1);
+      for (int i = 0; i < 4; ++i) {
+        const int c = q * 4 + i;
+        const int j = c & 7;
+        const uint32_t voff = ((c < 8 ? w_voff : x_voff) + (uint32_t)k0 * 2) | oob;
+        stage[c] = __builtin_amdgcn_raw_buffer_load_b128(c < 8 ? rW : rX, voff,
+                                                         j * (c < 8 ? w_rowstep : x_rowstep), 0);
       }
-      // issue pattern per sub-step: MFMA / DS-read pairs, then MFMAs interleaved with the
-      // fills and the global loads
+    };
+    auto store_q = [&](int buf, int q) __attribute__((always_inline)) {
+      uint8_t* wb = smem + buf * (2 * kTileBytes) + st_off;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int c = q * 4 + i;
+        *reinterpret_cast<u32x4*>(wb + (c < 8 ? 0 : kTileBytes) + (c & 7) * 4096) = stage[c];
       }
-      if constexpr (kk == 0) {
+    };
+
+
+    // Per-lane operand read offsets: row (lane % 32) of each 32-row block, logical chunk
+    // 2*kk + lane/32. Block bases are multiples of 32 rows, so the swizzle uses lane % 32.
+    const int a_row0 = wf * 128 + (lane & 31);
+    const int b_row0 = wt * 128 + (lane & 31);
+    uint32_t koff[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) koff[kk] = (uint32_t)((((kk * 2 + (lane >> 5)) ^ swz(lane & 31))) << 4);
+
+    bf16x8 fa[2][4], fb_[2][4];
+    auto read_frags = [&](int buf, int kk, bf16x8 (&af)[4], bf16x8 (&bf)[4]) __attribute__((always_inline)) {
+      const uint8_t* wb = smem + buf * (2 * kTileBytes);
+      const uint8_t* xb = wb + kTileBytes;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) af[f] = *reinterpret_cast<const bf16x8*>(wb + (a_row0 + f * 32) * 128 + koff[kk]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bf[t] = *reinterpret_cast<const bf16x8*>(xb + (b_row0 + t * 32) * 128 + koff[kk]);
+    };
+
+    // One K step s from LDS buffer s&1: the MFMAs of the step, the fill of buffer (s+1)&1
+    // from the stage set (data of step s+1), and the loads of step s+2 into the stage set.
+    // The fills and loads are done in sub-steps 0..2 and the step's one barrier comes after
+    // sub-step 2: by then every wave has read its last fragments of buffer s&1 and written its
+    // part of buffer (s+1)&1. Sub-step 3's MFMAs then run while the first fragments of step
+    // s+1 are read, so no fragment read waits behind the barrier. The fragments of sub-step 0
+    // arrive from the previous step (or the prologue). The last two steps fill and load past
+    // the end of K: those loads read zeros into a buffer that is not read again.
+    auto kstep = [&](int s) __attribute__((always_inline)) {
+      const int CUR = s & 1;
+      // sub-step kk is a compile-time constant so every register array index is static
+      auto sub = [&](auto kk_c) __attribute__((always_inline)) {
+        constexpr int kk = decltype(kk_c)::value;
+        // keep each sub-step's work together: at most one sub-step of fragments in flight
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kk < 3) read_frags(CUR, kk + 1, fa[(kk + 1) & 1], fb_[(kk + 1) & 1]);
+        else read_frags(CUR ^ 1, 0, fa[0], fb_[0]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][f], fb_[kk & 1][t], acc[f][t], 0, 0, 0);
+        // fills and loads: quarters 0 and 1 in sub-step 0, 2 in sub-step 1, 3 in sub-step 2
+        if constexpr (kk == 0) {
+          store_q(CUR ^ 1, 0);
+          store_q(CUR ^ 1, 1);
+          load_q((s + 2) * BK, 0);
+          load_q((s + 2) * BK, 1);
+        } else if constexpr (kk < 3) {
+          store_q(CUR ^ 1, kk + 1);
+          load_q((s + 2) * BK, kk + 1);
+        }
+        // issue pattern per sub-step: MFMA / DS-read pairs, then MFMAs interleaved with the
+        // fills and the global loads
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-      } else if constexpr (kk < 3) {
+        if constexpr (kk == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        }
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+        } else if constexpr (kk < 3) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      }
+      };
+      sub(std::integral_constant<int, 0>{});
+      sub(std::integral_constant<int, 1>{});
+      sub(std::integral_constant<int, 2>{});
+      __syncthreads();
+      sub(std::integral_constant<int, 3>{});
     };
-    sub(std::integral_constant<int, 0>{});
-    sub(std::integral_constant<int, 1>{});
-    sub(std::integral_constant<int, 2>{});
+
+    const int steps = (K + BK - 1) / BK;
+    // prologue: step 0 into LDS buffer 0, step 1 into the stage set, step 0's first fragments
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_q(0, q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store_q(0, q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_q(BK, q);
+    if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
     __syncthreads();
-    sub(std::integral_constant<int, 3>{});
-  };
+    read_frags(0, 0, fa[0], fb_[0]);
 
-  const int steps = (K + BK - 1) / BK;
-  // prologue: step 0 into LDS buffer 0, step 1 into the stage set, step 0's first fragments
-#pragma unroll
-  for (int q = 0; q < 4; ++q) load_q(0, q);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) store_q(0, q);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) load_q(BK, q);
-  if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
-  __syncthreads();
-  read_frags(0, 0, fa[0], fb_[0]);
-
-#pragma clang loop unroll(disable)
-  for (int s = 0; s < steps; ++s) kstep(s);
-  __syncthreads();  // every wave's last fragment reads are done before LDS is reused
+  #pragma clang loop unroll(disable)
+    for (int s = 0; s < steps; ++s) kstep(s);
+    __syncthreads();  // every wave's last fragment reads are done before LDS is reused
+  }
 
   if constexpr ((F & epi::kStatic) != 0) {
     // Epilogue on the accumulators in place; the mainloop's LDS buffers (128 KB) stage
@@ -249,17 +445,25 @@ constexpr uint32_t kCfgSwigluFp8 = epi::config(epi::kQuant, ACT_SWIGLU, FUSEDOPS
 constexpr uint32_t kCfgRscaleSwiglu = epi::config(epi::kRscale, ACT_SWIGLU, FUSEDOPS_BF16);
 constexpr uint32_t kCfgXent = epi::config(epi::kXent, ACT_NONE, FUSEDOPS_BF16);
 
+template <bool kDma>
 const void* t256_kernel_for(const EpiParams& e) {
   switch (epi::config_of(e)) {
-    case kCfgBiasGeluErf: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgBiasGeluErf>);
-    case kCfgBiasSplit: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgBiasSplit>);
-    case kCfgResidualRms: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgResidualRms>);
-    case kCfgSwiglu: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgSwiglu>);
-    case kCfgSwigluFp8: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgSwigluFp8>);
-    case kCfgRscaleSwiglu: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgRscaleSwiglu>);
-    case kCfgXent: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgXent>);
-    default: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<0>);
+    case kCfgBiasGeluErf: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgBiasGeluErf, kDma>);
+    case kCfgBiasSplit: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgBiasSplit, kDma>);
+    case kCfgResidualRms: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgResidualRms, kDma>);
+    case kCfgSwiglu: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgSwiglu, kDma>);
+    case kCfgSwigluFp8: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgSwigluFp8, kDma>);
+    case kCfgRscaleSwiglu: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgRscaleSwiglu, kDma>);
+    case kCfgXent: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgXent, kDma>);
+    default: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<0, kDma>);
   }
+}
+
+// The LDS-DMA mainloop needs whole W tiles and an even number of K steps.
+bool use_dma(const GemmArgs& a) { return a.N % BF == 0 && a.K % (2 * BK) == 0; }
+
+const void* kernel_for(const GemmArgs& a) {
+  return use_dma(a) ? t256_kernel_for<true>(a.ep) : t256_kernel_for<false>(a.ep);
 }
 
 }  // namespace
@@ -269,12 +473,12 @@ hipError_t launch_gemm_bf16_t256(GemmArgs a, hipStream_t stream) {
   a.tiles_f = (a.N + BF - 1) / BF;
   const int grid = a.tiles_t * a.tiles_f;
   void* args[] = {&a};
-  return hipLaunchKernel(t256_kernel_for(a.ep), dim3(grid), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(kernel_for(a), dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
 int gemm_bf16_t256_tile_t() { return BT; }
 int gemm_bf16_t256_tile_f() { return BF; }
 
-const void* gemm_bf16_t256_symbol(const EpiParams& e) { return t256_kernel_for(e); }
+const void* gemm_bf16_t256_symbol(const GemmArgs& a) { return kernel_for(a); }
 
 }  // namespace fusedops

@@ -10,11 +10,12 @@ struct GemmArgs;
 struct EpiParams;
 
 // bf16 GEMM + epilogue, 256 x 256 tiles (tokens x features), 4 waves. The kernel instance
-// depends on the epilogue configuration; the symbol is the one a call with `e` launches.
+// depends on the epilogue configuration and on the shape (whole W tiles and an even number
+// of K steps take the LDS-DMA mainloop); the symbol is the one a call with `a` launches.
 hipError_t launch_gemm_bf16_t256(GemmArgs a, hipStream_t stream);
 int gemm_bf16_t256_tile_t();
 int gemm_bf16_t256_tile_f();
-const void* gemm_bf16_t256_symbol(const EpiParams& e);
+const void* gemm_bf16_t256_symbol(const GemmArgs& a);
 
 // E4M3 inputs, 256 x 256 tiles (any M): v_mfma_scale_f32_32x32x64_f8f6f4 mainloop, the
 // dequantisation scales applied to the accumulators, then the same epilogues as above

@@ -257,7 +257,7 @@ def test_qkv_split_scaled_blocks_bit_exact():
     check_f32(np.hstack([q, k, v]), ref, "qkv f32")
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 528, 136), (17, 528, 72), (32, 2048, 256), (600, 1040, 64)])
+@pytest.mark.parametrize("M,N,K", [(300, 528, 136), (17, 528, 72), (32, 2048, 256), (600, 1040, 64), (600, 1024, 256)])
 def test_swiglu_fp8_rows(M, N, K):
     out = run_linear(M, N, K, act="swiglu", quant=True)
     # tier 2: the same kernel with an fp32 output gives the pre-quantisation values;
@@ -271,6 +271,29 @@ def test_swiglu_fp8_rows(M, N, K):
     check_fp8(host64(out["y"].view), s, y32, "codes vs own fp32 values")
     codes = host64(out["y"].view)
     assert all(((codes[m] & 0x7F) == 0x7E).any() for m in range(M) if s[m] > 0)
+
+
+# ---------------------------------------------------------------------------
+# The 256 x 256 kernel fills LDS by DMA when its W tiles and K steps are whole (N % 256 == 0,
+# K % 128 == 0; otherwise the register-staged mainloop runs): every epilogue instance on
+# ragged token tiles (M just past one tile, mid-tile), one to eight pairs of K steps. Those
+# DMAs leave LDS untouched where they read out of range, so ragged token rows are the case
+# that differs from the register-staged loads.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(129, 256, 128), (257, 256, 128), (300, 512, 384), (520, 768, 1024)])
+def test_dma_mainloop_bias_gelu_erf(M, N, K):
+    run_linear(M, N, K, bias=True, act="gelu_erf")
+
+
+def test_dma_mainloop_epilogue_instances():
+    run_linear(300, 768, 256, bias=True, split=3)                                       # fused QKV
+    run_linear(300, 512, 256, residual=True, aux=True, partials=True, gamma=True, seed=1)  # out-projection
+    run_linear(300, 512, 256, act="swiglu", seed=2)                                     # gate/up
+    run_linear(300, 512, 256, rscale=True, act="swiglu", seed=3)                        # gate/up after a row scale
+    run_linear(300, 512, 256, bias=True, act="gelu_tanh", out_dtype=I.F32, seed=4)      # generic instance
+    run_linear(300, 768, 256, bias=True, split=3, rope=64, seed=5)                      # generic, RoPE
+    run_linear(300, 512, 256, residual=True, gamma=True, inplace=True, pad=24, seed=6)  # in place, padded rows
 
 
 # ---------------------------------------------------------------------------
@@ -494,7 +517,7 @@ def run_pattern_a(M, d, K0, N2, *, act="swiglu", out_dtype=I.BF16, eps=1e-6, see
     return {"h2": h2, "p": p, "y": y, "W1": W1}
 
 
-@pytest.mark.parametrize("M,d,K0,N2", [(300, 264, 136, 528), (70, 256, 64, 512)])
+@pytest.mark.parametrize("M,d,K0,N2", [(300, 264, 136, 528), (70, 256, 64, 512), (300, 256, 128, 512)])
 def test_pattern_a_row_rms_swiglu(M, d, K0, N2):
     run_pattern_a(M, d, K0, N2)
 
@@ -571,7 +594,7 @@ def run_xent(M, N, K, *, store_logits=False, bias=False, act=None, in_dtype=I.BF
         check_lowp(host64(y.view), ref, "logits")
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 1000, 136), (17, 520, 40), (129, 4096, 64)])
+@pytest.mark.parametrize("M,N,K", [(300, 1000, 136), (17, 520, 40), (129, 4096, 64), (300, 1024, 256)])
 def test_xent_statistics_and_loss(M, N, K):
     run_xent(M, N, K)
 
