@@ -143,9 +143,10 @@ __device__ __forceinline__ int dtype_bytes(int dtype) {
 // form that gives 1 + erf(x) for x < 0 without cancellation.
 // GELU, erf form: 0.5 v (1 + erf(v / sqrt 2)) = v Phi(v). With a = |v| / sqrt 2 the same
 // formula gives h = 0.5 erfc(a) = t Q(t) 2^{-v^2 log2(e) / 2}, t = 1 / (1 + (p / sqrt 2)|v|),
-// Q holding the five coefficients halved; then Phi(v) = 1 - h for v >= 0 and h otherwise.
-// The constant factors are folded at compile time, leaving 13 VALU ops, one v_rcp_f32 and
-// one v_exp_f32 per element.
+// Q holding the five coefficients halved; then Phi(v) = 1 - h for v >= 0 and h otherwise,
+// so v Phi(v) = max(v, 0) - |v| h for either sign: no select, and for v < 0 the result is the
+// product |v| h itself (no cancellation in the negative tail). The constant factors are
+// folded at compile time, leaving 11 VALU ops, one v_rcp_f32 and one v_exp_f32 per element.
 __device__ __forceinline__ float gelu_erf_f32(float v) {
   constexpr double kRsqrt2 = 0.70710678118654752, kLog2e = 1.4426950408889634;
   constexpr float P = (float)(0.3275911 * kRsqrt2);
@@ -153,10 +154,11 @@ __device__ __forceinline__ float gelu_erf_f32(float v) {
                   A3 = (float)(0.5 * 1.421413741), A4 = (float)(0.5 * -1.453152027),
                   A5 = (float)(0.5 * 1.061405429);
   constexpr float E = (float)(-0.5 * kLog2e);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(fabsf(v), P, 1.0f));
+  const float a = fabsf(v);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(a, P, 1.0f));
   const float poly = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, A5, A4), A3), A2), A1);
   const float h = poly * __builtin_amdgcn_exp2f((v * E) * v);
-  return v * (v >= 0.f ? 1.0f - h : h);
+  return __builtin_fmaf(-a, h, fmaxf(v, 0.f));
 }
 
 // GELU, tanh form. 0.5 v (1 + tanh u) equals v / (1 + e^{-2u}), which needs one exp

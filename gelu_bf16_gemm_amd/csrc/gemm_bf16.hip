@@ -149,8 +149,9 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   };
 
   // One half-step region: MFMA i of the 32 (feature block J0 + i / 16, kk = i / 4 % 4, token
-  // block i % 4), read i of the region after MFMA i (reads first), DMAs at the positions
-  // below; sched barriers keep that order. rd(i) and dm(d) are the region's reads and DMAs.
+  // block i % 4), the region's fragment reads and DMAs spread between them at the positions
+  // below (a wave's LDS reads are latency-bound, so bursts stall the MFMAs); sched barriers
+  // keep that order. rd(i) and dm(d) are the region's reads and DMAs.
   auto region = [&](auto j0_c, auto nr_c, auto nd_c, const bf16x8 (&w)[2][4], const bf16x8 (&x)[4][4], auto&& rd,
                     auto&& dm) __attribute__((always_inline)) {
     constexpr int J0 = decltype(j0_c)::value, NR = decltype(nr_c)::value, ND = decltype(nd_c)::value;
@@ -159,7 +160,9 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
       constexpr int jb = i / 16, kk = (i / 4) % 4, tb = i % 4;
       __builtin_amdgcn_sched_barrier(0);
       acc[J0 + jb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[jb][kk], x[tb][kk], acc[J0 + jb][tb], 0, 0, 0);
-      if constexpr (i < NR) rd(i_c);
+      // reads spread evenly: 24 reads after MFMAs i % 4 != 3, 8 reads after every fourth
+      constexpr int r = NR == 24 ? ((i % 4) != 3 ? i - i / 4 : -1) : ((i % 4) == 0 && i / 4 < NR ? i / 4 : -1);
+      if constexpr (r >= 0) rd(std::integral_constant<int, r>{});
       // DMAs at positions 3, 11, 19, 27 (four) or at the odd positions 1, 3, .. (more)
       constexpr int d = ND == 4 ? ((i % 8) == 3 ? i / 8 : -1) : ((i & 1) && i / 2 < ND ? i / 2 : -1);
       if constexpr (d >= 0) dm(std::integral_constant<int, d>{});
