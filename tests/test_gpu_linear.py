@@ -257,7 +257,11 @@ def test_qkv_split_scaled_blocks_bit_exact():
     check_f32(np.hstack([q, k, v]), ref, "qkv f32")
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 528, 136), (17, 528, 72), (32, 2048, 256), (600, 1040, 64), (600, 1024, 256)])
+# (2300, 8192, 128) and (2300, 8200, 136): more 256 x 256 tiles than the device holds at once,
+# so tiles are handed out by ticket in row-block-major order (LDS-DMA and register-staged
+# mainloops; the last row block ragged, and ragged N in the second)
+@pytest.mark.parametrize("M,N,K", [(300, 528, 136), (17, 528, 72), (32, 2048, 256), (600, 1040, 64), (600, 1024, 256),
+                                   (2300, 8192, 128), (2300, 8200, 136)])
 def test_swiglu_fp8_rows(M, N, K):
     out = run_linear(M, N, K, act="swiglu", quant=True)
     # tier 2: the same kernel with an fp32 output gives the pre-quantisation values;
@@ -407,7 +411,7 @@ def test_fp8_tier1_exact_scales_and_codes():
     assert workspace_ok(ws)
 
 
-@pytest.mark.parametrize("M,N,K", [(40, 4160, 64), (300, 1056, 136)])
+@pytest.mark.parametrize("M,N,K", [(40, 4160, 64), (300, 1056, 136), (2300, 8192, 128)])
 def test_fp8_workspace_reused_across_calls(M, N, K):
     """One workspace, several quantised calls in a row on different inputs (the release
     flags count calls, the slots keep the previous call's maxima): every call is exact."""
