@@ -34,8 +34,8 @@ namespace epi {
 constexpr uint32_t kStatic = 1u << 31;
 constexpr uint32_t kBias = 1u << 0, kZ = 1u << 1, kAux = 1u << 2, kPart = 1u << 3, kGamma = 1u << 4,
                    kRscale = 1u << 5, kQuant = 1u << 6, kSplit = 1u << 7;
-// op lists with a RoPE rotation have no instance of their own (the generic one runs them);
-// cross-entropy statistics (kXent) do
+// RoPE rotations (kRope) have an instance for the fused QKV projection (bias + split) when
+// the head width divides the 256-feature tile; other RoPE op lists run the generic one
 constexpr uint32_t kRope = 1u << 20;
 constexpr uint32_t kXent = 1u << 21;
 constexpr int kActShift = 8, kYShift = 10, kZShift = 12, kAuxShift = 14, kBiasShift = 16, kGammaShift = 18;
@@ -78,6 +78,7 @@ struct Cfg {
   __device__ bool quant() const { if constexpr (S) return F & kQuant; else return e.quant != 0; }
   __device__ bool split() const { if constexpr (S) return F & kSplit; else return e.n_split != 0; }
   __device__ bool xent() const { if constexpr (S) return F & kXent; else return e.xent_labels != nullptr; }
+  __device__ bool rope() const { if constexpr (S) return F & kRope; else return e.rope_cs != nullptr; }
   __device__ int act() const { if constexpr (S) return (F >> kActShift) & 3; else return e.act; }
   __device__ int y_dt() const { if constexpr (S) return (F >> kYShift) & 3; else return e.y_dtype; }
   __device__ int z_dt() const { if constexpr (S) return (F >> kZShift) & 3; else return e.z_dtype; }
@@ -337,6 +338,54 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     dy.base[1] = dy.base[2] = nullptr;
     dy.ld = e.ldy;
     dy.split_w = 0;
+  }
+
+  if (fused && cfg.rope()) {
+    // RoPE on adjacent feature pairs after bias and activation ([Epilogue] §模式B: a pairwise
+    // map on the accumulators): a lane's group of four features f .. f+3 holds the pairs
+    // (f, f+1) and (f+2, f+3), whose cos / sin are the four floats at column f mod d of the
+    // token's table row (d divides the 256-feature tile, so f mod d = local feature mod d).
+    // Groups at or past rope_cols (V under a Q/K/V split) stay as computed; that test depends
+    // only on the feature, so it is uniform in a wave. Table rows past M read as zero.
+    if (cfg.bias()) {
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        const f32x16 b = feat(0, fb);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[fb][tb] += b;
+      }
+    }
+    const int rows = min(kTileRows, M - t0);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(e.rope_cs + (int64_t)t0 * e.rope_ld,
+                                                (uint32_t)(((int64_t)(rows - 1) * e.rope_ld + e.rope_d) * 4));
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      f32x4 c[4][4];  // [q][tb]: cos_i, sin_i, cos_i+1, sin_i+1
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          c[q][tb] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         rc, (uint32_t)((tk(tb) * e.rope_ld + (fl(fb, q) & (e.rope_d - 1))) * 4), 0, 0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (f0 + fl(fb, q) >= e.rope_cols) continue;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          f32x16& v = acc[fb][tb];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float x0 = v[4 * q + 2 * j], x1 = v[4 * q + 2 * j + 1];
+            const float cs = c[q][tb][2 * j], sn = c[q][tb][2 * j + 1];
+            v[4 * q + 2 * j] = x0 * cs - x1 * sn;
+            v[4 * q + 2 * j + 1] = x0 * sn + x1 * cs;
+          }
+        }
+      }
+    }
+    emit(ydt, pairs, dy, [&](int fb, int tb) __attribute__((always_inline)) { return acc[fb][tb]; });
+    return;
   }
 
   if (fused) {

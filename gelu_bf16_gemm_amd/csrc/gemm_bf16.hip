@@ -436,9 +436,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
 }
 
 // Epilogue configurations with an instance of their own (the op sets of the fused QKV
-// projection, MLP-up, out-projection, gate/up, FP8 gate/up, gate/up after a deferred RMSNorm,
-// and the LM head with cross-entropy statistics); any other op list runs the generic instance,
-// which reads its choices at run time.
+// projection, with and without RoPE, MLP-up, out-projection, gate/up, FP8 gate/up, gate/up
+// after a deferred RMSNorm, and the LM head with cross-entropy statistics); any other op list
+// runs the generic instance, which reads its choices at run time.
 constexpr uint32_t kCfgBiasGeluErf = epi::config(epi::kBias, ACT_GELU_ERF, FUSEDOPS_BF16);
 constexpr uint32_t kCfgBiasSplit = epi::config(epi::kBias | epi::kSplit, ACT_NONE, FUSEDOPS_BF16);
 constexpr uint32_t kCfgResidualRms = epi::config(epi::kZ | epi::kAux | epi::kPart | epi::kGamma, ACT_NONE,
@@ -447,6 +447,12 @@ constexpr uint32_t kCfgSwiglu = epi::config(0, ACT_SWIGLU, FUSEDOPS_BF16);
 constexpr uint32_t kCfgSwigluFp8 = epi::config(epi::kQuant, ACT_SWIGLU, FUSEDOPS_F8E4M3);
 constexpr uint32_t kCfgRscaleSwiglu = epi::config(epi::kRscale, ACT_SWIGLU, FUSEDOPS_BF16);
 constexpr uint32_t kCfgXent = epi::config(epi::kXent, ACT_NONE, FUSEDOPS_BF16);
+constexpr uint32_t kCfgBiasSplitRope = epi::config(epi::kBias | epi::kSplit | epi::kRope, ACT_NONE, FUSEDOPS_BF16);
+
+// The RoPE instance reads the table at column (local feature mod d): d must divide the tile.
+bool rope_fits(const EpiParams& e) {
+  return e.rope_d <= 128 && BF % e.rope_d == 0 && e.rope_ld * 4 * BT < (int64_t(1) << 31);
+}
 
 template <bool kDma>
 const void* t256_kernel_for(const EpiParams& e) {
@@ -458,6 +464,9 @@ const void* t256_kernel_for(const EpiParams& e) {
     case kCfgSwigluFp8: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgSwigluFp8, kDma>);
     case kCfgRscaleSwiglu: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgRscaleSwiglu, kDma>);
     case kCfgXent: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgXent, kDma>);
+    case kCfgBiasSplitRope:
+      if (rope_fits(e)) return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<kCfgBiasSplitRope, kDma>);
+      return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<0, kDma>);
     default: return reinterpret_cast<const void*>(&gemm_bf16_t256_kernel<0, kDma>);
   }
 }

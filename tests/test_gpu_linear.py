@@ -355,6 +355,13 @@ def test_rope_qkv_split(M, N, K):
     run_linear(M, N, K, bias=True, split=3, rope=64)
 
 
+@pytest.mark.parametrize("d", [8, 128, 256])
+def test_rope_head_widths(d):
+    """Head widths that divide the 256-feature tile (8, 128) rotate on the accumulators; 256
+    runs the row-layout chain. Ragged last token tile: table rows past M are never used."""
+    run_linear(300, 768, 256, bias=True, split=3, rope=d, seed=7)
+
+
 def test_rope_full_width_after_activation():
     run_linear(129, 512, 64, act="gelu_tanh", rope=128)
     run_linear(300, 264, 136, bias=True, rope=8, out_dtype=I.F32, seed=1)
