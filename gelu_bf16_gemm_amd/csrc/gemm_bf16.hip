@@ -69,9 +69,10 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 
 // Mainloop fed by LDS DMA (buffer loads that write LDS directly: no staging registers and no
 // ds_write), for tiles whose W rows and K steps are all whole (N % 256 == 0, K % 128 == 0;
-// checked on the host). Out-of-range lanes of an LDS DMA leave LDS untouched instead of
-// writing zeros, so X rows past M are read from the tile's last valid row instead (their
-// outputs are never stored and no reduction mixes rows).
+// checked on the host). An LDS DMA instruction whose lanes are all out of range leaves LDS
+// untouched instead of writing zeros, so ragged token tiles do not rely on out-of-range reads:
+// X rows past M are read from the tile's last valid row instead (their outputs are never stored
+// and no reduction mixes rows).
 //
 // Buffers: W and X tiles of a step (256 rows x 128 bytes each, the swizzled layout of
 // tile256.h), two of each. A step is walked in two regions: A multiplies feature blocks 0-1
