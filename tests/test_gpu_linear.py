@@ -301,6 +301,28 @@ def test_dma_mainloop_epilogue_instances():
 
 
 # ---------------------------------------------------------------------------
+# Few tokens (M <= 128, the few-token kernel) at decode-like widths and depths: ragged token
+# tiles, a single token, K up to 2048, every epilogue path.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(17, 512, 256), (1, 64, 2048), (33, 1024, 2048), (128, 192, 768)])
+def test_few_token_bias_gelu(M, N, K):
+    run_linear(M, N, K, bias=True, act="gelu_erf")
+
+
+def test_few_token_epilogue_paths():
+    run_linear(100, 1024, 512, residual=True, aux=True, partials=True, gamma=True, seed=1)
+    run_linear(64, 2048, 1280, act="swiglu", seed=2)
+    run_linear(96, 768, 512, bias=True, split=3, rope=64, seed=3)
+    run_linear(50, 512, 256, bias=True, act="gelu_tanh", out_dtype=I.F32, seed=4)
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 4096, 2048), (77, 1152, 768)])
+def test_few_token_fp8_rows(M, N, K):
+    run_linear(M, N, K, act="swiglu", quant=True)
+
+
+# ---------------------------------------------------------------------------
 # E4M3 inputs, scale-after-accumulate: the 256 x 256 E4M3 kernel for every M; K = 160 and 272
 # end in a partial 128-code step, K = 16 is a single 16-code chunk.
 # ---------------------------------------------------------------------------
