@@ -182,6 +182,30 @@ def fusedops_linear_epilogue(x, w, y, *, bias=None, ops=(), workspace=None, out_
         _ptr(y), _ld(y) if y is not None else 0, od, _ptr(workspace), ws_bytes, _stream(stream))
 
 
+def prepare_linear_epilogue(x, w, y, *, bias=None, ops=(), workspace=None, out_dtype=None, stream=None):
+    """The arguments of one fusedops_linear_epilogue call, marshalled once; the returned function
+    makes exactly that call and returns its status. For launch loops, where marshalling every
+    call would take longer than a small kernel runs. The stream is the one current now unless
+    given; the tensors must stay alive and unchanged in shape while the function is used."""
+    M, K = x.shape
+    N = w.shape[0]
+    arr, n = op_array(list(ops))
+    od = out_dtype if out_dtype is not None else (dtype_code(y) if y is not None else None)
+    if od is None:
+        split = [o for o in ops if o.kind == OP_SPLIT_COLS]
+        od = split[0].dtype if split else F32
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), _ptr(bias), M, N, K, dtype_code(x), arr, n,
+            _ptr(y), _ld(y) if y is not None else 0, od, _ptr(workspace), ws_bytes, _stream(stream))
+    fn = lib.fusedops_linear_epilogue
+
+    def call() -> int:
+        return fn(*args)
+
+    call.keep = (x, w, y, bias, workspace, arr)  # the buffers and the op array live as long as call
+    return call
+
+
 def fusedops_layernorm_gelu(x, y, gamma=None, beta=None, *, eps: float = 1e-5, gelu_form: int = GELU_TANH,
                             stream=None) -> int:
     rows, cols = x.shape

@@ -295,8 +295,8 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
     kern = (M <= 128 && !op_par && big_tiles < 256) ? Kernel::SKINNY : Kernel::T256;
   }
   const bool big = kern == Kernel::T256 || kern == Kernel::FP8;  // the 256 x 256 tile kernels
-  const int tile_rows = big ? 256 : (kern == Kernel::SKINNY ? 64 : 128);
-  const int tile_tok = big ? 256 : (kern == Kernel::SKINNY ? 32 : 64);
+  const int tile_rows = big ? 256 : (kern == Kernel::SKINNY ? 64 : 128);  // at most, for the fp32 kernel
+  const int tile_tok = big ? 256 : 32;                                     // few-token and fp32 kernels
   // 32-bit buffer offsets cover one tile's rows (operands, and the residual rows the
   // 256 x 256 kernel copies into LDS)
   if (((int64_t)(tile_rows - 1) * ldw + K) * es_in >= (int64_t(1) << 31) ||
@@ -362,11 +362,12 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (ol.quant) {
     const int tile_f = kern == Kernel::T256 ? gemm_bf16_t256_tile_f()
                        : kern == Kernel::FP8 ? gemm_fp8_t256_tile_f()
-                       : kern == Kernel::SKINNY ? gemm_bf16_skinny_tile_f() : gemm_f32_tile_f();
+                       : kern == Kernel::SKINNY ? gemm_bf16_skinny_tile_f() : gemm_f32_tile_f(a);
     const void* sym = kern == Kernel::T256 ? gemm_bf16_t256_symbol(a)
                       : kern == Kernel::FP8 ? gemm_fp8_t256_symbol(a.ep)
-                      : kern == Kernel::SKINNY ? gemm_bf16_skinny_symbol() : gemm_f32_symbol();
-    const int threads = kern == Kernel::SKINNY ? gemm_bf16_skinny_threads() : 256;
+                      : kern == Kernel::SKINNY ? gemm_bf16_skinny_symbol() : gemm_f32_symbol(a);
+    const int threads = kern == Kernel::SKINNY ? gemm_bf16_skinny_threads()
+                        : kern == Kernel::F32 ? gemm_f32_threads() : 256;
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||

@@ -31,11 +31,13 @@ int gemm_bf16_skinny_tile_f();
 int gemm_bf16_skinny_threads();
 const void* gemm_bf16_skinny_symbol();
 
-// fp32 GEMM + epilogue (v_mfma_f32_32x32x2_f32), 64-token x 128-feature tiles.
+// fp32 GEMM + epilogue (v_mfma_f32_32x32x2_f32), 32-token x 64-feature tiles (128 features
+// when the op list writes RMSNorm row partials), K split over the 8 waves of a workgroup.
 hipError_t launch_gemm_f32(GemmArgs a, hipStream_t stream);
 int gemm_f32_tile_t();
-int gemm_f32_tile_f();
-const void* gemm_f32_symbol();
+int gemm_f32_tile_f(const GemmArgs& a);
+int gemm_f32_threads();
+const void* gemm_f32_symbol(const GemmArgs& a);
 
 struct LnArgs {
   const void* x; int64_t ldx;

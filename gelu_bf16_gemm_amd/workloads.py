@@ -74,6 +74,7 @@ class LinearRun:
         else:
             self.y = torch.empty((M, self.n_out), dtype=_TORCH[self.out_dtype], device=dev)
         self.ops_by_copy = [self._ops(i) for i in range(copies)]
+        self._calls, self._calls_stream = None, None
         self.ws = None
         if quant:
             nbytes = B.fusedops_linear_workspace_bytes(M, N, K, self.ops_by_copy[0])
@@ -114,10 +115,19 @@ class LinearRun:
         return ops
 
     def launch(self, i: int = 0, stream=None) -> None:
-        """One pass of the workload (input copy i % copies)."""
+        """One pass of the workload (input copy i % copies). On the current stream the calls are
+        marshalled once per copy, so a launch loop is not bounded by per-call marshalling."""
         i %= self.copies
-        B.check(B.fusedops_linear_epilogue(self.X[i], self.W[i], self.y, bias=self.b, ops=self.ops_by_copy[i],
-                                           workspace=self.ws, out_dtype=self.out_dtype, stream=stream))
+        if stream is None:
+            if self._calls is None or self._calls_stream != torch.cuda.current_stream():
+                self._calls_stream = torch.cuda.current_stream()
+                self._calls = [B.prepare_linear_epilogue(self.X[c], self.W[c], self.y, bias=self.b,
+                                                         ops=self.ops_by_copy[c], workspace=self.ws,
+                                                         out_dtype=self.out_dtype) for c in range(self.copies)]
+            B.check(self._calls[i]())
+        else:
+            B.check(B.fusedops_linear_epilogue(self.X[i], self.W[i], self.y, bias=self.b, ops=self.ops_by_copy[i],
+                                               workspace=self.ws, out_dtype=self.out_dtype, stream=stream))
         if self.partials is not None:
             B.check(B.fusedops_rmsnorm_finalize(self.partials, self.N, self.eps, self.r, stream=stream))
         if self.xent is not None:

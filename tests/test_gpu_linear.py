@@ -480,7 +480,8 @@ def test_fp32_linear_gelu_full_size():
     assert y.intact()
 
 
-@pytest.mark.parametrize("M,N,K", [(70, 136, 36), (1, 8, 4)])
+# (100, 200, 600): three K chunks of 256, the last one ragged; ragged token and feature tiles
+@pytest.mark.parametrize("M,N,K", [(70, 136, 36), (1, 8, 4), (100, 200, 600)])
 def test_fp32_path_ops(M, N, K):
     run_linear(M, N, K, in_dtype=I.F32, out_dtype=I.F32, bias=True, residual=True, aux=True, partials=True,
                gamma=True, act="gelu_erf")
