@@ -230,27 +230,12 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   dma_wait_barrier<0>();  // every DMA has landed and every fragment read is done before LDS is reused
 }
 
+// One output tile (token tile tt, feature tile ft): mainloop and epilogue.
 template <uint32_t F, bool kDma>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];  // [stage][W, X]
-  __shared__ __attribute__((aligned(16))) float svec[4 * 256];               // epilogue vectors
-  __shared__ int slot[2];
-
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uint8_t* smem, float* svec, int* slot) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wf = wave >> 1, wt = wave & 1;
-
-  int tt, ft;
-  if (a.ep.quant && a.ep.tickets) {
-    // FP8 row scales need every feature tile of a token block: hand out tiles in
-    // row-block-major ticket order so no block waits on a tile that is not running.
-    const int ticket = draw_ticket(a.ep.ws, a.tiles_t * a.tiles_f, slot);
-    tt = ticket / a.tiles_f;
-    ft = ticket - tt * a.tiles_f;
-    if (tt >= a.tiles_t) return;  // a workspace that was not zero-filled: touch nothing
-  } else {
-    tile_coords(blockIdx.x, a.tiles_t, a.tiles_f, tt, ft);
-  }
   const int f0 = ft * BF, t0 = tt * BT;
   const int K = a.K;
 
@@ -436,6 +421,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   }
 }
 
+template <uint32_t F, bool kDma>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];  // [stage][W, X]
+  __shared__ __attribute__((aligned(16))) float svec[4 * 256];               // epilogue vectors
+  __shared__ int slot[2];
+
+  if (a.ep.quant) {
+    int tt, ft;
+    if (a.ep.tickets) {
+      // FP8 row scales need every feature tile of a token block: hand out tiles in
+      // row-block-major ticket order so no block waits on a tile that is not running.
+      const int ticket = draw_ticket(a.ep.ws, a.tiles_t * a.tiles_f, slot);
+      tt = ticket / a.tiles_f;
+      ft = ticket - tt * a.tiles_f;
+      if (tt >= a.tiles_t) return;  // a workspace that was not zero-filled: touch nothing
+    } else {
+      tile_coords(blockIdx.x, a.tiles_t, a.tiles_f, tt, ft);
+    }
+    gemm_tile<F, kDma>(a, tt, ft, smem, svec, slot);
+    return;
+  }
+  // Resident workgroups walk the tiles: workgroup b takes tile ids b, b + grid, ... (the same
+  // XCD each time, in the XCD-aware order), so a tile's first loads are issued while the
+  // previous tile's stores are still in flight, and no workgroup launch sits between tiles.
+  const int tiles = a.tiles_t * a.tiles_f;
+#pragma clang loop unroll(disable)
+  for (int id = blockIdx.x; id < tiles; id += gridDim.x) {
+    // the previous tile's epilogue is done with LDS (its global stores may still be in flight)
+    if (id != (int)blockIdx.x) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    int tt, ft;
+    tile_coords(id, a.tiles_t, a.tiles_f, tt, ft);
+    gemm_tile<F, kDma>(a, tt, ft, smem, svec, slot);
+  }
+}
+
 // Epilogue configurations with an instance of their own (the op sets of the fused QKV
 // projection, with and without RoPE, MLP-up, out-projection, gate/up, FP8 gate/up, gate/up
 // after a deferred RMSNorm, and the LM head with cross-entropy statistics); any other op list
@@ -484,7 +504,17 @@ const void* kernel_for(const GemmArgs& a) {
 hipError_t launch_gemm_bf16_t256(GemmArgs a, hipStream_t stream) {
   a.tiles_t = (a.M + BT - 1) / BT;
   a.tiles_f = (a.N + BF - 1) / BF;
-  const int grid = a.tiles_t * a.tiles_f;
+  const int tiles = a.tiles_t * a.tiles_f;
+  // without FP8 row scales, one resident workgroup per CU walks the tiles (a multiple of the 8
+  // XCDs, so each workgroup stays on one XCD's tile range)
+  int grid = tiles;
+  if (!a.ep.quant) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus >= 8 &&
+        tiles > cus)
+      grid = cus / 8 * 8;
+  }
   void* args[] = {&a};
   return hipLaunchKernel(kernel_for(a), dim3(grid), dim3(kThreads), args, 0, stream);
 }

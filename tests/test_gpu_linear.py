@@ -290,6 +290,14 @@ def test_dma_mainloop_bias_gelu_erf(M, N, K):
     run_linear(M, N, K, bias=True, act="gelu_erf")
 
 
+# more tiles than CUs: resident workgroups walk several tiles each (LDS-DMA and register-staged
+# mainloops, ragged last token tile, ragged N in the second)
+@pytest.mark.parametrize("M,N,K", [(2300, 8192, 128), (2300, 8200, 136)])
+def test_tile_walking_workgroups(M, N, K):
+    run_linear(M, N, K, bias=True, act="gelu_erf", seed=11)
+    run_linear(M, N, K, residual=True, aux=True, partials=True, gamma=True, seed=12)
+
+
 def test_dma_mainloop_epilogue_instances():
     run_linear(300, 768, 256, bias=True, split=3)                                       # fused QKV
     run_linear(300, 512, 256, residual=True, aux=True, partials=True, gamma=True, seed=1)  # out-projection
