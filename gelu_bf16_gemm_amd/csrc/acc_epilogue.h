@@ -240,7 +240,7 @@ __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int r
 // `svec` the tile's vectors (VecPrefetch); every thread of the workgroup must call this.
 template <uint32_t F>
 __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, const float* svec,
-                                             int t0, int f0, int rb, int ft, int* slot) {
+                                             int t0, int f0, int ft, int* slot) {
   using namespace accepi;
   const EpiParams& e = a.ep;
   const epi::Cfg<F> cfg{e};
@@ -268,7 +268,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     const int R = kTileRows / passes;
 #pragma clang loop unroll(disable)
     for (int p = 0; p < passes; ++p) {
-      __syncthreads();
+      lds_barrier();  // earlier stores may still drain
       if (passes == 1 || wt == p) {
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
@@ -284,7 +284,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
             }
           }
       }
-      __syncthreads();
+      lds_barrier();
       copy_out(lds, R, C, t0 + p * R, M, d);
     }
   };
@@ -430,7 +430,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
 #pragma clang loop unroll(disable)
     for (int p = 0; p < passes; ++p) {
       const int rows = min(R, M - t0 - p * R);  // valid rows of this pass (>= 1 for p = 0)
-      __syncthreads();
+      lds_barrier();
       if (rows > 0) {
         const uint8_t* zb = static_cast<const uint8_t*>(e.z) + ((int64_t)(t0 + p * R) * e.ldz + f0) * es;
         const __amdgpu_buffer_rsrc_t rz =
@@ -450,7 +450,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
           *reinterpret_cast<u32x4*>(lds + id * 16) = u32x4{0, 0, 0, 0};
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
-      __syncthreads();
+      lds_barrier();
       if (passes == 1 || wt == p) {
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
@@ -585,8 +585,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     const int i = threadIdx.x, t = t0 + i;
     if (t < M) publish_row_amax(e, ft, t, fmaxf(s_half[i], s_half[kTileRows + i]));
   }
-  rendezvous_wait(e, rb, ft, a.tiles_f);
-  reduce_row_amax<kTileRows>(e, a.tiles_f, t0, min(kTileRows, M - t0), s_amax);
+  rendezvous_row_amax<kTileRows>(e, ft, a.tiles_f, t0, min(kTileRows, M - t0), s_amax, slot);
   __syncthreads();
   {
     const int i = threadIdx.x, t = t0 + i;

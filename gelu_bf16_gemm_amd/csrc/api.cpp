@@ -79,15 +79,19 @@ int32_t parse_ops(const fusedops_op* ops, int32_t n_ops, OpList& out) {
   return FUSEDOPS_OK;
 }
 
-// FP8 workspace: a control record per row block of the finest token tile (32 tokens) with
-// one 128-byte line per counter (groups of 16 column tiles of the finest feature tile, 64
-// features), and per token one absmax slot per column tile, rounded up to a multiple of 4
-// slots so each token's slots start 16-byte aligned.
-int64_t ws_row_blocks(int64_t M) { return cdiv(M, 32); }
+// FP8 workspace: a 32-word header, then one record per block of 32 tokens (the finest token
+// tile): a control record with one 128-byte line per counter (groups of 16 column tiles of
+// the finest feature tile, 64 features), then per token one absmax slot per column tile and
+// one per group, each run rounded up to a multiple of 4 slots so it starts 16-byte aligned.
+// A record's size depends on N only, so calls with the same N may share a workspace.
 int64_t ws_slots_per_token(int64_t N) { return cdiv(cdiv(N, 64), 4) * 4; }
 int64_t ws_groups(int64_t N) { return cdiv(cdiv(N, 64), 16); }
+int64_t ws_group_slots_per_token(int64_t N) { return cdiv(ws_groups(N), 4) * 4; }
+int64_t ws_block_words(int64_t N) {
+  return 32 * (2 + ws_groups(N)) + 32 * ws_slots_per_token(N) + 32 * ws_group_slots_per_token(N);
+}
 size_t ws_bytes_for(int64_t M, int64_t N) {
-  const int64_t words = 32 + 32 * (2 + ws_groups(N)) * ws_row_blocks(M) + M * ws_slots_per_token(N);
+  const int64_t words = 32 + cdiv(M, 32) * ws_block_words(N);
   return (size_t)(cdiv(words * 4, 256) * 256);
 }
 
@@ -275,6 +279,7 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
 
   // ---- workspace
   if (ol.quant) {
+    if (ws_bytes_for(M, N) > 0xFFFFFFFFu) return FUSEDOPS_ERR_UNSUPPORTED;  // the kernels address it in 32 bits
     if (!workspace || workspace_bytes < ws_bytes_for(M, N) || !aligned(workspace, 16)) return FUSEDOPS_ERR_WORKSPACE;
     const Span sw{reinterpret_cast<uintptr_t>(workspace),
                   reinterpret_cast<uintptr_t>(workspace) + workspace_bytes, true};
@@ -343,9 +348,11 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   if (op_q) {
     e.scales = static_cast<float*>(op_q->out);
     e.ws = static_cast<uint32_t*>(workspace);
-    e.ws_rb = (int)ws_row_blocks(M);
+    e.ws_bytes = (uint32_t)ws_bytes_for(M, N);
+    e.ws_bs = (int)ws_block_words(N);
     e.ws_s = (int)ws_slots_per_token(N);
     e.ws_g = (int)ws_groups(N);
+    e.ws_gs = (int)ws_group_slots_per_token(N);
   }
   e.y = Y; e.ldy = ldy; e.y_dtype = out_dtype;
   if (op_split) {

@@ -39,6 +39,11 @@ __device__ __forceinline__ u32x4 buffer_load_16B(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
 
+// Workgroup barrier that orders LDS use only: this wave's LDS reads and writes have completed,
+// but its global stores may still be in flight (__syncthreads' release fence would also wait
+// for those, s_waitcnt vmcnt(0)). For reusing an LDS buffer while earlier stores drain.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // conversions (round to nearest even everywhere)
 // ---------------------------------------------------------------------------

@@ -51,9 +51,11 @@ struct EpiParams {
   int quant;              // FP8 per-row quantised writeback
   float* scales;
   uint32_t* ws;           // rendezvous workspace (quant only)
-  int ws_rb;              // row-block counters reserved in the workspace
-  int ws_s;               // absmax slots per token in the workspace
-  int ws_g;               // column-tile groups per row-block control record
+  uint32_t ws_bytes;      //   its size
+  int ws_bs;              //   words per 32-token block record
+  int ws_s;               //   absmax slots per token (one per 64-feature column tile)
+  int ws_g;               //   column-tile groups per control record
+  int ws_gs;              //   group absmax slots per token
   int tickets;            // hand out tiles by ticket (the grid exceeds what is resident at once)
   void* y;                int64_t ldy;     int y_dtype;
   int n_split;            int64_t split_w; int64_t ldv;
@@ -86,17 +88,24 @@ constexpr int kEpiThreads = 256;
 // Workspace layout (uint32 words):
 //   [0]                error word: set to 1 if a wait ever hit its spin bound (never cleared here)
 //   [1]                tile ticket counter (back at zero after every call)
-//   [32 + CR rb ...]   control record of row block rb, CR = 32 (2 + G) words, one counter per
-//                      128-byte line: line 0 counts arriving groups, line 1 is the release
-//                      flag (a generation count: it goes up by one per call), line 2 + g counts
-//                      the arrivals of column-tile group g (kGroupTiles tiles each; G = ws_g)
-//   [B, ...)           row absmax slots, float bits, from B = 32 + CR R, S words per token
-//                      (S = ws_s, a multiple of 4): word B + t*S + ft holds the absmax of
-//                      token t over the features of column tile ft
-// Each tile writes its own slots; no two tiles touch the same word. The arrival counters
-// are reset by the tile that completes them, and the flag is only ever compared with the
-// value a tile saw before arriving, so nothing needs clearing after a call: the workspace
-// must be zero-filled once after allocation and then handed to every call unchanged.
+//   [32 + BS b, ...)   record of the 32-token block b (tokens 32 b .. 32 b + 31), BS = ws_bs words:
+//     control lines    32 (2 + G) words, one counter per 128-byte line, used by the row block
+//                      of a tile whose first token is 32 b: line 0 counts arriving groups,
+//                      line 1 is the release flag (a generation count: it goes up by one per
+//                      call), line 2 + g counts the arrivals of column-tile group g
+//                      (kGroupTiles tiles each; G = ws_g)
+//     tile slots       S words per token (S = ws_s, a multiple of 4): word ft of token t holds
+//                      the absmax of token t over the features of column tile ft
+//     group slots      GS words per token (GS = ws_gs, a multiple of 4): word g of token t
+//                      holds its absmax over column-tile group g
+// The records depend on N only, so calls with the same N (and any M up to the size the
+// workspace was made for) may share one. Each tile writes its own slots and the last tile
+// to arrive in a group writes the group's slots; no two tiles touch the same word. Readers
+// take only the words of the current call (a run's words past the valid count may hold
+// another call's values). The arrival counters are reset by the tile that completes them,
+// and the flag is only ever compared with the value a tile saw before arriving, so nothing
+// needs clearing after a call: the workspace must be zero-filled once after allocation and
+// then handed to every call unchanged.
 //
 // Memory ordering. Each XCD has its own L2; agent-scope release / acquire fences are
 // L2-wide write-back / invalidate operations that would disturb every other tile on the XCD.
@@ -110,42 +119,57 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kGroupTiles = 16;
 constexpr int kPolicyCoherent = 16;  // sc1: agent-scope coherence policy of a buffer access
 
-__device__ __forceinline__ uint32_t* ws_ctl(const EpiParams& e, int rb) {
-  return e.ws + 32 + 32 * (2 + e.ws_g) * rb;
+// Word offsets in the workspace: the record of token t's block, the control record of the row
+// block starting at token t0 (a multiple of 32), token t's tile slots and its group slots.
+__device__ __forceinline__ int64_t ws_block(const EpiParams& e, int t) { return 32 + (int64_t)(t >> 5) * e.ws_bs; }
+__device__ __forceinline__ uint32_t* ws_ctl(const EpiParams& e, int t0) { return e.ws + ws_block(e, t0); }
+__device__ __forceinline__ int64_t ws_slot_word(const EpiParams& e, int t) {
+  return ws_block(e, t) + 32 * (2 + e.ws_g) + (t & 31) * e.ws_s;
 }
-__device__ __forceinline__ uint32_t* ws_slots(const EpiParams& e) {
-  return e.ws + 32 + 32 * (2 + e.ws_g) * e.ws_rb;
+__device__ __forceinline__ int64_t ws_gslot_word(const EpiParams& e, int t) {
+  return ws_block(e, t) + 32 * (2 + e.ws_g) + 32 * e.ws_s + (t & 31) * e.ws_gs;
 }
 
 // Publish the absmax m of token t over column tile ft.
 __device__ __forceinline__ void publish_row_amax(const EpiParams& e, int ft, int t, float m) {
-  __hip_atomic_store(ws_slots(e) + (int64_t)t * e.ws_s + ft, __float_as_uint(m), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(e.ws + ws_slot_word(e, t) + ft, __float_as_uint(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// After the row block's rendezvous: out[i] = absmax of token t0 + i over all `tiles_f`
-// column tiles, for i < nrows. ROWS rows (a power of two dividing the 256 threads) share the
-// workgroup: 256 / ROWS threads per row, each taking 16-byte runs of the row's slots with
-// all of its loads in flight. Slots past tiles_f in a row are never written, so zero.
-template <int ROWS>
-__device__ __forceinline__ void reduce_row_amax(const EpiParams& e, int tiles_f, int t0, int nrows, float* out) {
+// Maximum of the workspace words [w, w + count) of each of `nrows` rows (w = run(i) for row i,
+// 16-byte aligned), read at the coherence point. ROWS rows (a power of two dividing the 256
+// threads) share the workgroup, 256 / ROWS threads per row, each taking 16-byte runs with all
+// of its loads in flight; words of a run past `count` are ignored. Every thread of row `row`
+// gets the row's maximum (absmax values: non-negative floats order like their bit patterns).
+template <int ROWS, typename Run>
+__device__ __forceinline__ uint32_t coherent_row_max(const EpiParams& e, Run&& run, int count, int nrows, int& row) {
   constexpr int TPR = 256 / ROWS;
   static_assert(TPR >= 1 && TPR <= 64 && 256 % ROWS == 0, "threads per row");
-  const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(ws_slots(e) + (int64_t)t0 * e.ws_s, (uint32_t)(nrows * e.ws_s * 4));
-  uint32_t m = 0;  // non-negative floats order like their bit patterns
+  row = threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(e.ws, e.ws_bytes);
+  uint32_t m = 0;
   if (row < nrows) {
-#pragma unroll 8
-    for (int j = part * 4; j < tiles_f; j += TPR * 4) {
-      const u32x4 v = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((row * e.ws_s + j) * 4), 0, kPolicyCoherent));
-      m = max(m, max(max(v[0], v[1]), max(v[2], v[3])));
+    const uint32_t w = (uint32_t)run(row);
+    // batches of 8 runs: all loads in flight before the first is used
+    constexpr int kBatch = 8;
+    for (int j0 = part * 4; j0 < count; j0 += kBatch * TPR * 4) {
+      u32x4 v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int j = j0 + b * TPR * 4;
+        v[b] = j < count ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (w + j) * 4u, 0,
+                                                                                           kPolicyCoherent))
+                         : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = j0 + b * TPR * 4 + i < count ? max(m, v[b][i]) : m;
     }
   }
 #pragma unroll
   for (int o = 1; o < TPR; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
-  if (row < nrows && part == 0) out[row] = __uint_as_float(m);
+  return m;
 }
 
 // Take the next tile ticket (thread 0 draws, the block shares it through LDS). The block
@@ -163,28 +187,61 @@ __device__ __forceinline__ int draw_ticket(uint32_t* ws, int total, int* lds_slo
   return t;
 }
 
-// Arrive at row block `rb` as column tile ft and wait until all `need` column tiles of the
-// block have arrived (every tile publishes its absmax slots first). Arrivals are counted in
-// groups of kGroupTiles on separate lines, so no counter sees more than a few dozen
-// atomics; the tile that completes the last group raises the block's flag. The wait is
-// bounded; on timeout the error word is set.
-__device__ __forceinline__ void rendezvous_wait(const EpiParams& e, int rb, int ft, int need) {
+// Arrive at the row block starting at token t0 as column tile ft of `need` (this tile's slots
+// for its rows are published), wait until every column tile of the block has arrived, and return in out[i]
+// the absmax of token t0 + i over all of them (i < nrows; ROWS as for coherent_row_max).
+// Arrivals are counted in groups of kGroupTiles tiles on separate lines, so no counter sees
+// more than a few dozen atomics; the tile that completes the last group raises the block's
+// flag. With 128 or more rows per tile the last tile to arrive in a group first folds the
+// group's slots into the group slot of each token, and every tile then reads only the group
+// slots (a few words per token instead of one per column tile): for 256-row tiles that is
+// 4 KB of reads per tile instead of 64 KB, at the price of two more round trips to the
+// coherence point on the last arrival's path, which is why few-row tiles (decode, where the
+// one rendezvous is the kernel's tail) read the tile slots directly. The wait is bounded; on
+// timeout the error word is set.
+template <int ROWS>
+__device__ __forceinline__ void rendezvous_row_amax(const EpiParams& e, int ft, int need, int t0, int nrows,
+                                                    float* out, int* lds_slot) {
+  constexpr int TPR = 256 / ROWS;
+  constexpr bool kTwoLevel = ROWS >= 128;
   __builtin_amdgcn_s_waitcnt(0);  // this thread's slot stores have completed
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t* rec = ws_ctl(e, rb);
-    uint32_t* flag = rec + 32;
-    const uint32_t gen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int g = ft / kGroupTiles, groups = (need + kGroupTiles - 1) / kGroupTiles;
-    const int in_group = min(kGroupTiles, need - g * kGroupTiles);
-    uint32_t* gc = rec + 64 + 32 * g;
-    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)in_group - 1) {
-      __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__hip_atomic_fetch_add(rec, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)groups - 1) {
-        __hip_atomic_store(rec, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(flag, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+  uint32_t* rec = ws_ctl(e, t0);
+  uint32_t* flag = rec + 32;
+  const int g = ft / kGroupTiles, groups = (need + kGroupTiles - 1) / kGroupTiles;
+  const int in_group = min(kGroupTiles, need - g * kGroupTiles);
+  auto arrive_block = [&](uint32_t gen) {
+    if (__hip_atomic_fetch_add(rec, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)groups - 1) {
+      __hip_atomic_store(rec, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(flag, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  };
+  uint32_t gen = 0;
+  if (threadIdx.x == 0) {
+    gen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* gc = rec + 64 + 32 * g;
+    const bool last = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      (uint32_t)in_group - 1;
+    if (last) __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (kTwoLevel) *lds_slot = last ? 1 : 0;
+    else if (last) arrive_block(gen);  // the group's arrival, straight away
+  }
+  if constexpr (kTwoLevel) {
+    __syncthreads();
+    if (*lds_slot) {
+      // every tile of the group has published: its maxima per token go to the group slot,
+      // then the group arrives at the block
+      int row;
+      const uint32_t m = coherent_row_max<ROWS>(
+          e, [&](int i) { return ws_slot_word(e, t0 + i) + g * kGroupTiles; }, in_group, nrows, row);
+      if (row < nrows && threadIdx.x % TPR == 0)
+        __hip_atomic_store(e.ws + ws_gslot_word(e, t0 + row) + g, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);  // the group slot stores have completed
+      __syncthreads();
+      if (threadIdx.x == 0) arrive_block(gen);
+    }
+  }
+  if (threadIdx.x == 0) {
     uint32_t it = 0;
     while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
       __builtin_amdgcn_s_sleep(1);
@@ -195,6 +252,13 @@ __device__ __forceinline__ void rendezvous_wait(const EpiParams& e, int rb, int 
     }
   }
   __syncthreads();
+  int row;
+  uint32_t m;
+  if constexpr (kTwoLevel)
+    m = coherent_row_max<ROWS>(e, [&](int i) { return ws_gslot_word(e, t0 + i); }, groups, nrows, row);
+  else
+    m = coherent_row_max<ROWS>(e, [&](int i) { return ws_slot_word(e, t0 + i); }, need, nrows, row);
+  if (row < nrows && threadIdx.x % TPR == 0) out[row] = __uint_as_float(m);
 }
 
 // ---------------------------------------------------------------------------
@@ -458,7 +522,7 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
 // after every column tile of the token block has done so, to quantise.
 template <int COLS, int NSRC, int ROWS, int PASSES, typename StageFn>
 __device__ __forceinline__ void run_staged_epilogue(const GemmArgs& a, float* tile, int t0, int f0,
-                                                    int nrows_total, int rb, int ft, int* lds_slot,
+                                                    int nrows_total, int ft, int* lds_slot,
                                                     float* lds_amax, StageFn&& stage) {
   const EpiParams& e = a.ep;
   const int rounds = e.quant ? 2 : 1;
@@ -466,9 +530,8 @@ __device__ __forceinline__ void run_staged_epilogue(const GemmArgs& a, float* ti
 #pragma clang loop unroll(disable)
   for (int round = 0; round < rounds; ++round) {
     if (round == 1) {
-      rendezvous_wait(e, rb, ft, a.tiles_f);
-      // every column tile of the row block has published: reduce this tile's rows once
-      reduce_row_amax<ROWS * PASSES>(e, a.tiles_f, t0, nrows_total, lds_amax);
+      // every column tile of the row block publishes: this tile's rows' maxima, once
+      rendezvous_row_amax<ROWS * PASSES>(e, ft, a.tiles_f, t0, nrows_total, lds_amax, lds_slot);
     }
     const int mode = e.quant ? (round == 0 ? EPI_AMAX : EPI_QUANT) : EPI_STORE;
 #pragma clang loop unroll(disable)

@@ -403,14 +403,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uin
   if constexpr ((F & epi::kStatic) != 0) {
     // Epilogue on the accumulators in place; the mainloop's LDS buffers (128 KB) stage
     // the finished values for coalesced stores.
-    acc_epilogue<F>(a, acc, smem, svec, t0, f0, tt, ft, slot);
+    acc_epilogue<F>(a, acc, smem, svec, t0, f0, ft, slot);
   } else {
     // Any other op list: the fp32 tile is staged through LDS in two 128-token passes
     // (128 KB each; pass p takes the accumulators of the waves with wt == p) and the
     // row-layout chain reads every choice at run time.
     __shared__ float s_amax[BT];
     run_staged_epilogue<BF, 1, 128, 2>(
-        a, reinterpret_cast<float*>(smem), t0, f0, min(BT, a.M - t0), tt, ft, slot, s_amax,
+        a, reinterpret_cast<float*>(smem), t0, f0, min(BT, a.M - t0), ft, slot, s_amax,
         [&](int p, float* tile) __attribute__((always_inline)) {
           if (wt != p) return;
 #pragma unroll
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
 #pragma clang loop unroll(disable)
   for (int id = blockIdx.x; id < tiles; id += gridDim.x) {
     // the previous tile's epilogue is done with LDS (its global stores may still be in flight)
-    if (id != (int)blockIdx.x) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (id != (int)blockIdx.x) lds_barrier();
     int tt, ft;
     tile_coords(id, a.tiles_t, a.tiles_f, tt, ft);
     gemm_tile<F, kDma>(a, tt, ft, smem, svec, slot);

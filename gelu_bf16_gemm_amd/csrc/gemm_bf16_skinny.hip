@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_skinny_kernel(GemmArgs 
   }
   __syncthreads();
 
-  run_staged_epilogue<BF, 4, BT, 1>(a, reinterpret_cast<float*>(lds), t0, f0, min(BT, a.M - t0), tt, ft, slot,
+  run_staged_epilogue<BF, 4, BT, 1>(a, reinterpret_cast<float*>(lds), t0, f0, min(BT, a.M - t0), ft, slot,
                                     s_amax, [&](int, float* tile) {
                                       stage_block<BF>(tile + kq * BT * BF, acc, fb * 32, 0);
                                     });

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32_kernel(GemmArgs a) {
   }
   __syncthreads();  // LDS is reused for the partial tiles
 
-  run_staged_epilogue<BF, kWaves, BT, 1>(a, lds, t0, f0, x_rows, tt, ft, slot, s_amax, [&](int, float* tile) {
+  run_staged_epilogue<BF, kWaves, BT, 1>(a, lds, t0, f0, x_rows, ft, slot, s_amax, [&](int, float* tile) {
     float* part = tile + wave * BT * BF;
 #pragma unroll
     for (int b = 0; b < FB; ++b) stage_block<BF>(part, acc[b], 32 * b, 0);

@@ -271,11 +271,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_t256_kernel(GemmArgs a) 
   }
 
   if constexpr ((F & epi::kStatic) != 0) {
-    acc_epilogue<F>(a, acc, smem, svec, t0, f0, tt, ft, slot);
+    acc_epilogue<F>(a, acc, smem, svec, t0, f0, ft, slot);
   } else {
     __shared__ float s_amax[BT];
     run_staged_epilogue<BF, 1, 128, 2>(
-        a, reinterpret_cast<float*>(smem), t0, f0, min(BT, a.M - t0), tt, ft, slot, s_amax,
+        a, reinterpret_cast<float*>(smem), t0, f0, min(BT, a.M - t0), ft, slot, s_amax,
         [&](int p, float* tile) __attribute__((always_inline)) {
           if (wt != p) return;
 #pragma unroll

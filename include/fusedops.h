@@ -183,14 +183,18 @@ typedef struct fusedops_op {
  *   workspace / workspace_bytes
  *          Device scratch of at least fusedops_linear_workspace_bytes(...) bytes, 16-byte
  *          aligned (0 bytes when no op needs one; then workspace may be NULL). Only
- *          QUANT_FP8_ROW uses it: per 32-token row block, arrival counters and a release flag
+ *          QUANT_FP8_ROW uses it: per 32-token block, arrival counters and a release flag
  *          for the row rendezvous, and per token one absmax slot per 64-feature column tile
- *          (about 4 * M * N / 64 bytes in all). Zero-fill it once after allocation, then pass
- *          it unchanged to every call: the library keeps state in it between calls (release
- *          flags count calls; slots hold the last call's maxima). Its first 32-bit word is an
- *          error word the kernels set to 1 if a row rendezvous ever gave up waiting (the
- *          quantised output of that call is then unreliable); the library never clears it.
- *          Calls that may run concurrently (different streams) must not share a workspace.
+ *          and one per group of 16 such tiles (about 4 * M * N / 64 bytes in all; a call
+ *          needing more than 4 GiB returns UNSUPPORTED). Zero-fill it once after allocation,
+ *          then pass it unchanged to every call: the library keeps state in it between calls
+ *          (release flags count calls; slots hold the last call's maxima). Its layout depends
+ *          on N only: calls with the same N and any M up to the one it was sized for may share
+ *          it (say decode and prefill of one layer); calls with different N need workspaces of
+ *          their own. Its first 32-bit word is an error word the kernels set to 1 if a row
+ *          rendezvous ever gave up waiting (the quantised output of that call is then
+ *          unreliable); the library never clears it. Calls that may run concurrently
+ *          (different streams) must not share a workspace.
  *   stream hipStream_t.
  * Outputs are written in fp32 -> out dtype with round-to-nearest-even.
  * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE, LAUNCH (see enum).

@@ -473,6 +473,35 @@ def test_fp8_workspace_reused_across_calls(M, N, K):
         check_fp8(host64(y), s, v, f"call {call} codes")
 
 
+def test_fp8_workspace_shared_across_token_counts():
+    """One workspace shared by calls with the same N and different M: a few-token call (64-wide
+    column tiles, 20 per row) with large values, then a 600-token call on the 256-wide tile
+    kernel (5 column tiles, so a 16-byte slot run holds words it must not use), then the
+    few-token call again. The workspace records depend on N only; every call's scales are exact
+    and no rendezvous gives up."""
+    rng = np.random.default_rng(23)
+    N, K = 1280, 128
+    ws = torch.zeros(B.fusedops_linear_workspace_bytes(600, N, K, [B.op(B.OP_SWIGLU), B.op(B.OP_QUANT_FP8_ROW)]) // 4,
+                     dtype=torch.int32, device="cuda")
+    for call, (M, std) in enumerate([(32, 50.0), (600, 1.0), (600, 0.5), (32, 3.0)]):
+        s_out = torch.empty(M, dtype=torch.float32, device="cuda")
+        ops = [B.op(B.OP_SWIGLU), B.op(B.OP_QUANT_FP8_ROW, out=s_out)]
+        X = I.random_stored(rng, (M, K), I.BF16, std=std)
+        W = I.random_stored(rng, (N, K), I.BF16, std=K ** -0.5)
+        Xd, Wd = dev(X, I.BF16), dev(W, I.BF16)
+        y = torch.empty((M, N // 2), dtype=torch.uint8, device="cuda")
+        y32 = torch.empty((M, N // 2), dtype=torch.float32, device="cuda")
+        note(f"fp8 workspace shared, call {call}: M={M} N={N} K={K}")
+        assert B.fusedops_linear_epilogue(Xd, Wd, y, ops=ops, workspace=ws, out_dtype=I.F8E4M3) == B.OK
+        assert B.fusedops_linear_epilogue(Xd, Wd, y32, ops=[B.op(B.OP_SWIGLU)]) == B.OK
+        torch.cuda.synchronize()
+        assert workspace_ok(ws), f"call {call}"
+        v = host64(y32)
+        s = host64(s_out).astype(np.float32)
+        assert np.array_equal(s, O.fp8_row_scale(np.abs(v).max(axis=1).astype(np.float32))), f"call {call}"
+        check_fp8(host64(y), s, v, f"call {call} codes")
+
+
 def test_fp32_linear_gelu_full_size():
     """The fp32 workload at its full size: X 64x256, W 256x256, b 256, GELU(erf)."""
     spec = I.WORKLOADS["linear_gelu_f32_64x256x256"]
