@@ -112,13 +112,18 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   uint32_t w_lane[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) w_lane[g] = (uint32_t)(l8 * a.ldw * 2 + ((p8 ^ l8 ^ g) << 4));
-  // X: wave w fills rows w * 64 + g * 8 .., g = 0..7 (rows past M read row M - 1)
-  uint32_t x_lane[8];
+  // X: token half h of the tile is token blocks 2h and 2h + 1 of both 128-token halves (what
+  // every wave reads for those blocks); wave w fills its rows x_row0(h) + g * 8 .., g = 0..3
+  // (rows past M read row M - 1)
+  auto x_row0 = [&](int h) __attribute__((always_inline)) { return (wave >> 1) * 128 + (2 * h + (wave & 1)) * 32; };
+  uint32_t x_lane[2][4];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int r = min(wave * 64 + g * 8 + l8, x_rows - 1);
-    x_lane[g] = (uint32_t)(r * a.ldx * 2 + ((p8 ^ l8 ^ (g & 1)) << 4));
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r = min(x_row0(h) + g * 8 + l8, x_rows - 1);
+      x_lane[h][g] = (uint32_t)(r * a.ldx * 2 + ((p8 ^ l8 ^ (g & 1)) << 4));
+    }
   // DMAs of steps past the last read nothing (the offset's top bit puts them out of range)
   // and leave LDS as it is; they are still issued so that the wait counts stay exact.
   auto dma_w1 = [&](int t, int j, int g) __attribute__((always_inline)) {
@@ -126,15 +131,15 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
     const int r0 = w_row0 + j * 32 + g * 8;
     lds_dma16(rW, w_lane[g] | oob, (uint32_t)(r0 * a.ldw * 2 + t * BK * 2), lds0 + (t & 1) * kBuf + r0 * 128);
   };
-  auto dma_x1 = [&](int t, int g) __attribute__((always_inline)) {
+  auto dma_x1 = [&](int t, int h, int g) __attribute__((always_inline)) {
     const uint32_t oob = t < steps ? 0u : kOobOffset;
-    lds_dma16(rX, x_lane[g] | oob, (uint32_t)(t * BK * 2),
-              lds0 + (t & 1) * kBuf + kTileBytes + (wave * 64 + g * 8) * 128);
+    lds_dma16(rX, x_lane[h][g] | oob, (uint32_t)(t * BK * 2),
+              lds0 + (t & 1) * kBuf + kTileBytes + (x_row0(h) + g * 8) * 128);
   };
   auto dma_w = [&](int t, int j) __attribute__((always_inline)) { dma_w1(t, j, 0); dma_w1(t, j, 1); };
-  auto dma_x = [&](int t, int half) __attribute__((always_inline)) {
+  auto dma_x = [&](int t, int h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) dma_x1(t, half * 4 + g);
+    for (int g = 0; g < 4; ++g) dma_x1(t, h, g);
   };
 
   // Operand fragments: row (lane % 32) of a 32-row block, logical chunk 2 kk + lane / 32.
@@ -150,64 +155,68 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   };
 
   // One half-step region: MFMA i of the 32 (feature block J0 + i / 16, kk = i / 4 % 4, token
-  // block i % 4), the region's fragment reads and DMAs spread between them at the positions
-  // below (a wave's LDS reads are latency-bound, so bursts stall the MFMAs); sched barriers
-  // keep that order. rd(i) and dm(d) are the region's reads and DMAs.
-  auto region = [&](auto j0_c, auto nr_c, auto nd_c, const bf16x8 (&w)[2][4], const bf16x8 (&x)[4][4], auto&& rd,
-                    auto&& dm) __attribute__((always_inline)) {
-    constexpr int J0 = decltype(j0_c)::value, NR = decltype(nr_c)::value, ND = decltype(nd_c)::value;
+  // block i % 4), with the region's 16 fragment reads after the even MFMAs and its 8 DMAs
+  // after MFMAs 1, 5, .., 29 (a wave's LDS reads are latency-bound, so bursts stall the
+  // MFMAs); sched barriers keep that order. rd(q) and dm(d) are the region's reads and DMAs.
+  auto region = [&](auto j0_c, const bf16x8 (&w)[2][4], const bf16x8 (&x)[4][4], auto&& rd, auto&& dm)
+                    __attribute__((always_inline)) {
+    constexpr int J0 = decltype(j0_c)::value;
     static_for<0, 32>([&](auto i_c) __attribute__((always_inline)) {
       constexpr int i = decltype(i_c)::value;
       constexpr int jb = i / 16, kk = (i / 4) % 4, tb = i % 4;
       __builtin_amdgcn_sched_barrier(0);
       acc[J0 + jb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[jb][kk], x[tb][kk], acc[J0 + jb][tb], 0, 0, 0);
-      // reads spread evenly: 24 reads after MFMAs i % 4 != 3, 8 reads after every fourth
-      constexpr int r = NR == 24 ? ((i % 4) != 3 ? i - i / 4 : -1) : ((i % 4) == 0 && i / 4 < NR ? i / 4 : -1);
-      if constexpr (r >= 0) rd(std::integral_constant<int, r>{});
-      // DMAs at positions 3, 11, 19, 27 (four) or at the odd positions 1, 3, .. (more)
-      constexpr int d = ND == 4 ? ((i % 8) == 3 ? i / 8 : -1) : ((i & 1) && i / 2 < ND ? i / 2 : -1);
-      if constexpr (d >= 0) dm(std::integral_constant<int, d>{});
+      if constexpr (i % 2 == 0) rd(std::integral_constant<int, i / 2>{});
+      if constexpr (i % 4 == 1) dm(std::integral_constant<int, i / 4>{});
     });
     __builtin_amdgcn_sched_barrier(0);
   };
-  using C4 = std::integral_constant<int, 4>;
-  using C8 = std::integral_constant<int, 8>;
-  using C12 = std::integral_constant<int, 12>;
-  using C24 = std::integral_constant<int, 24>;
 
   // Step s with X fragments in set P (the next step's go to set P ^ 1). Region A multiplies
-  // feature blocks 0-1 (W fragments in wfr[0]) and reads blocks 2-3 and all of X of s+1;
-  // region B multiplies blocks 2-3 and reads blocks 0-1 of s+1.
+  // feature blocks 0-1 (W fragments in wfr[0]) and reads W blocks 2-3 of s and X token blocks
+  // 0-1 of s+1; region B multiplies blocks 2-3 and reads W blocks 0-1 and X token blocks 2-3
+  // of s+1. Each region reads 16 KB per wave and issues 8 DMAs; every DMA lands 1.5 steps
+  // before its data is read.
   auto step = [&](auto p_c, int s) __attribute__((always_inline)) {
     constexpr int P = decltype(p_c)::value;
-    // A: DMA W blocks 0-1 of s+2 (their space was read in B of s-1)
-    region(std::integral_constant<int, 0>{}, C24{}, C4{}, wfr[0], xf[P],
+    // A: DMA W blocks 0-1 of s+2 (read in B of s-1) and X token half 1 of s+2 (read in B of s-1)
+    region(std::integral_constant<int, 0>{}, wfr[0], xf[P],
            [&](auto r) __attribute__((always_inline)) {
              constexpr int q = decltype(r)::value;
              if constexpr (q < 8) wfr[1][q / 4][q % 4] = frag(s, false, a_row0 + (2 + q / 4) * 32, q % 4);
              else xf[P ^ 1][(q - 8) / 4][(q - 8) % 4] = frag(s + 1, true, b_row0 + ((q - 8) / 4) * 32, (q - 8) % 4);
            },
-           [&](auto d) __attribute__((always_inline)) { dma_w1(s + 2, decltype(d)::value / 2, decltype(d)::value % 2); });
-    dma_wait_barrier<16>();  // next: W blocks 0-1 of s+1 (region A of s-1)
-    // B: DMA W blocks 2-3 of s+2 and X of s+3 (their space was read in A of s)
-    region(std::integral_constant<int, 2>{}, C8{}, C12{}, wfr[1], xf[P],
+           [&](auto d) __attribute__((always_inline)) {
+             constexpr int q = decltype(d)::value;
+             if constexpr (q < 4) dma_w1(s + 2, q / 2, q % 2);
+             else dma_x1(s + 2, 1, q - 4);
+           });
+    dma_wait_barrier<16>();  // next: W blocks 0-1 and X token half 1 of s+1 (region A of s-1)
+    // B: DMA W blocks 2-3 of s+2 and X token half 0 of s+3 (both read in A of s)
+    region(std::integral_constant<int, 2>{}, wfr[1], xf[P],
            [&](auto r) __attribute__((always_inline)) {
              constexpr int q = decltype(r)::value;
-             wfr[0][q / 4][q % 4] = frag(s + 1, false, a_row0 + (q / 4) * 32, q % 4);
+             if constexpr (q < 8) wfr[0][q / 4][q % 4] = frag(s + 1, false, a_row0 + (q / 4) * 32, q % 4);
+             else
+               xf[P ^ 1][2 + (q - 8) / 4][(q - 8) % 4] =
+                   frag(s + 1, true, b_row0 + (2 + (q - 8) / 4) * 32, (q - 8) % 4);
            },
            [&](auto d) __attribute__((always_inline)) {
              constexpr int q = decltype(d)::value;
              if constexpr (q < 4) dma_w1(s + 2, 2 + q / 2, q % 2);
-             else dma_x1(s + 3, q - 4);
+             else dma_x1(s + 3, 0, q - 4);
            });
-    dma_wait_barrier<16>();  // next: W blocks 2-3 of s+1 and X of s+2 (region B of s-1)
+    dma_wait_barrier<16>();  // next: W blocks 2-3 of s+1 and X token half 0 of s+2 (region B of s-1)
   };
 
-  // Prologue: the DMAs of steps 0 and 1 in the loop's own order (X of step 0 first), the
-  // fragments of step 0, then the rest of that order up to the end of step -1.
+  // Prologue: X and W blocks 0-1 of step 0, then the loop's own DMA order from region B of
+  // step -2 (W blocks 2-3 of step 0, X half 0 of step 1) and region A of step -1 (W blocks
+  // 0-1 and X half 1 of step 1); the fragments of step 0; region B of step -1 (W blocks 2-3 of
+  // step 1, X half 0 of step 2, into space the step-0 fragments were read from).
   dma_x(0, 0); dma_x(0, 1);
-  dma_w(0, 0); dma_w(0, 1); dma_w(0, 2); dma_w(0, 3); dma_x(1, 0); dma_x(1, 1);
-  dma_w(1, 0); dma_w(1, 1);
+  dma_w(0, 0); dma_w(0, 1);
+  dma_w(0, 2); dma_w(0, 3); dma_x(1, 0);
+  dma_w(1, 0); dma_w(1, 1); dma_x(1, 1);
   if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
   dma_wait_barrier<16>();  // X and W blocks 0-1 of step 0
 #pragma unroll
@@ -219,8 +228,8 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) wfr[0][jb][kk] = frag(0, false, a_row0 + jb * 32, kk);
   dma_wait_barrier<40>();  // every wave holds its step-0 fragments: X buffer 0 and W blocks 0-1 are free
-  dma_w(1, 2); dma_w(1, 3); dma_x(2, 0); dma_x(2, 1);
-  dma_wait_barrier<16>();  // W blocks 2-3 of step 0 and X of step 1
+  dma_w(1, 2); dma_w(1, 3); dma_x(2, 0);
+  dma_wait_barrier<16>();  // W blocks 2-3 of step 0 and X half 0 of step 1
 
 #pragma clang loop unroll(disable)
   for (int s = 0; s < steps; s += 2) {
