@@ -77,12 +77,13 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 // Buffers: W and X tiles of a step (256 rows x 128 bytes each, the swizzled layout of
 // tile256.h), two of each. A step is walked in two regions: A multiplies feature blocks 0-1
 // (W rows wf*128 + 0..63 of each wave's half), B blocks 2-3, each wave against its 128 tokens,
-// whose fragments for the whole step sit in registers (read in region A of the previous step).
-// A region reads the W fragments the next region multiplies, so W blocks 2-3 of a buffer are
-// free after A and blocks 0-1 after B, and X is free once its fragments are in registers.
-// Each region ends with a barrier after which the space just freed is refilled by DMA with
-// data two steps ahead. Per wave and step the DMAs are (2 instructions per W block, 8 for X)
-//   region A: W blocks 0-1 of s+2        region B: W blocks 2-3 of s+2, X of s+3
+// whose fragments for the whole step sit in registers (read during the previous step: token
+// blocks 0-1 in region A, 2-3 in region B). A region reads the W fragments the next region
+// multiplies, so after A W blocks 2-3 of a buffer and X token half 0 (token blocks 0-1 of
+// both 128-token halves) are free, after B W blocks 0-1 and X token half 1. Each region ends
+// with a barrier after which the space just freed is refilled by DMA with data two steps
+// ahead. Per wave and step the DMAs are (2 instructions per W block, 4 per X half)
+//   region A: W blocks 0-1, X half 1 of s+2        region B: W blocks 2-3 of s+2, X half 0 of s+3
 // so every DMA has 1.5 steps to land, and each is paired with an MFMA: the four waves leave a
 // barrier together, and DMAs issued back to back would queue at the CU's address unit while
 // the matrix core idles. Each barrier waits for exactly the DMAs the next region reads; the
