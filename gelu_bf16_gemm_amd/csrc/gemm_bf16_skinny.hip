@@ -87,7 +87,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_skinny_kernel(GemmArgs 
     const uint32_t k0 = (uint32_t)(s < stages ? (s + ft) % stages : s) * KS;
     const uint32_t oob = (uint32_t)(k0 + lc * 8 >= (uint32_t)K) << 31;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wreg[d][i] = buffer_load_16B(rW, (w_voff[i] + k0 * 2) | oob);
+    for (int i = 0; i < 4; ++i)  // each W byte is read once: nontemporal
+      wreg[d][i] = __builtin_amdgcn_raw_buffer_load_b128(rW, (w_voff[i] + k0 * 2) | oob, 0, kNonTemporal);
   };
   auto load_x = [&](int s, int d) __attribute__((always_inline)) {
     const uint32_t k0 = (uint32_t)(s < stages ? (s + ft) % stages : s) * KS;
