@@ -236,6 +236,22 @@ def test_quant_rules_and_workspace():
     assert B.fusedops_linear_workspace_bytes(0, 64, 64, [sw, q]) == 0
 
 
+def test_quant_workspace_limit():
+    """The kernels address the FP8 workspace in 32 bits: a call that would need more than
+    4 GiB of it is refused as unsupported (here M = 2^20 tokens, N = 2^17 features: about
+    4 M N / 64 bytes = 8 GiB), before anything is enqueued."""
+    M, N, K = 1 << 20, 1 << 17, 64
+    q = mkop(B.OP_QUANT_FP8_ROW, dtype=B.F32, out=addr(6))
+    sw = mkop(B.OP_SWIGLU)
+    need = B.fusedops_linear_workspace_bytes(M, N, K, [sw, q])
+    assert need > (1 << 32)
+    assert lin(X=addr(0), W=addr(1), M=M, N=N, K=K, ops=[sw, q], Y=addr(16), ldy=N // 2, out_dt=B.F8E4M3,
+               ws=addr(40), ws_bytes=need) == B.ERR_UNSUPPORTED
+    # a quarter of the tokens fits
+    need_q = B.fusedops_linear_workspace_bytes(M // 4, N, K, [sw, q])
+    assert 0 < need_q < (1 << 32)
+
+
 def test_aliasing_rules():
     # Y inside X
     assert lin(Y=addr(0, 64)) == B.ERR_INVALID_ARG
