@@ -355,31 +355,50 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
         for (int tb = 0; tb < 4; ++tb) acc[fb][tb] += b;
       }
     }
-    const int rows = min(kTileRows, M - t0);
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(e.rope_cs + (int64_t)t0 * e.rope_ld,
-                                                (uint32_t)(((int64_t)(rows - 1) * e.rope_ld + e.rope_d) * 4));
+    if (f0 < e.rope_cols) {
+      // The tile's table rows (tokens t0 .., rope_d floats each) are copied into LDS by DMA in
+      // the staged-tile layout (16-byte chunk c of row r at position c ^ (r mod min(C, 32))),
+      // with every wave instruction filling 1 KB of consecutive positions; each lane then reads
+      // its 16-byte (cos, sin, cos, sin) runs from LDS, free of bank conflicts for rope_d >= 64.
+      // Table rows past M are not read (their outputs are never stored).
+      const int rows = min(kTileRows, M - t0);
+      const int C = e.rope_d >> 2;  // 16-byte chunks per table row (rope_d a power of two >= 8)
+      const int cshift = __builtin_ctz(C);
+      const int m = (C < 32 ? C : 32) - 1;
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(e.rope_cs + (int64_t)t0 * e.rope_ld,
+                                                  (uint32_t)(((int64_t)(rows - 1) * e.rope_ld + e.rope_d) * 4));
+      const int lane_u = threadIdx.x & 63;
+#pragma unroll 8
+      for (int j = 0; j < C; ++j) {  // kTileRows * C chunks, kEpiThreads per instruction round
+        const int id = j * kEpiThreads + wave * 64 + lane_u;
+        const int r = id >> cshift, pos = id & (C - 1);
+        const int c = pos ^ (r & m);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(lds + (j * kEpiThreads + wave * 64) * 16), 16,
+                                                 (uint32_t)((r * e.rope_ld + c * 4) * 4), 0, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+      lds_barrier();
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-      f32x4 c[4][4];  // [q][tb]: cos_i, sin_i, cos_i+1, sin_i+1
+      for (int fb = 0; fb < 4; ++fb) {
+        f32x4 cs4[4][4];  // [q][tb]: cos_i, sin_i, cos_i+1, sin_i+1
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-          c[q][tb] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                         rc, (uint32_t)((tk(tb) * e.rope_ld + (fl(fb, q) & (e.rope_d - 1))) * 4), 0, 0));
+          for (int tb = 0; tb < 4; ++tb)
+            cs4[q][tb] = *reinterpret_cast<const f32x4*>(lds + st_off(tk(tb), (fl(fb, q) & (e.rope_d - 1)) * 4, C));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (f0 + fl(fb, q) >= e.rope_cols) continue;
+        for (int q = 0; q < 4; ++q) {
+          if (f0 + fl(fb, q) >= e.rope_cols) continue;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          f32x16& v = acc[fb][tb];
+          for (int tb = 0; tb < 4; ++tb) {
+            f32x16& v = acc[fb][tb];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float x0 = v[4 * q + 2 * j], x1 = v[4 * q + 2 * j + 1];
-            const float cs = c[q][tb][2 * j], sn = c[q][tb][2 * j + 1];
-            v[4 * q + 2 * j] = x0 * cs - x1 * sn;
-            v[4 * q + 2 * j + 1] = x0 * sn + x1 * cs;
+            for (int j = 0; j < 2; ++j) {
+              const float x0 = v[4 * q + 2 * j], x1 = v[4 * q + 2 * j + 1];
+              const float cs = cs4[q][tb][2 * j], sn = cs4[q][tb][2 * j + 1];
+              v[4 * q + 2 * j] = x0 * cs - x1 * sn;
+              v[4 * q + 2 * j + 1] = x0 * sn + x1 * cs;
+            }
           }
         }
       }
