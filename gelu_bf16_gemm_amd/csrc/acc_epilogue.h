@@ -533,13 +533,17 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
       // 4 hb + j sits in register 4 q + j of block fb
       const int o = __float_as_int(svec[768 + tk(tb)]) - wbase;  // label, fetched before the mainloop
       const bool mine = o >= 0 && o < 128 && wbase + o < N && ((o >> 2) & 1) == hb;
-      const int want = (o >> 5) * 16 + ((o >> 3) & 3) * 4 + (o & 3);  // fb * 16 + r
-      float tv = 0.f;
+      // a token's label lies in one column tile of its row, so most waves hold none: the
+      // register select runs only when some lane of the wave holds its label (uniform test)
+      if (__ballot(mine) != 0) {
+        const int want = (o >> 5) * 16 + ((o >> 3) & 3) * 4 + (o & 3);  // fb * 16 + r
+        float tv = 0.f;
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
+        for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tv = want == fb * 16 + r ? acc[fb][tb][r] : tv;
-      if (mine) e.xent_tgt[t] = tv;
+          for (int r = 0; r < 16; ++r) tv = want == fb * 16 + r ? acc[fb][tb][r] : tv;
+        if (mine) e.xent_tgt[t] = tv;
+      }
       // columns at or past N (last tile only, a wave-uniform test) become -inf: they drop out
       // of the maximum, and e^-inf = 0 out of the sum; they are never stored
       if (wbase + 128 > N) {
