@@ -344,6 +344,24 @@ def test_fp8_input_residual():
     run_linear(300, 264, 160, in_dtype=I.F8E4M3, residual=True)
 
 
+# Whole 256-wide W tiles and whole 128-code K steps: ragged token tiles, 2 to 6 K steps, and
+# 288 tiles (more than there are CUs) for both static instances and the generic one.
+@pytest.mark.parametrize("M,N,K", [(300, 512, 256), (520, 256, 768), (2300, 8192, 256)])
+def test_fp8_input_whole_tiles_bias_gelu(M, N, K):
+    run_linear(M, N, K, in_dtype=I.F8E4M3, bias=True, act="gelu_erf")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 512, 512), (2300, 8192, 256)])
+def test_fp8_input_whole_tiles_residual(M, N, K):
+    run_linear(M, N, K, in_dtype=I.F8E4M3, residual=True)
+
+
+def test_fp8_input_whole_tiles_generic_chain():
+    run_linear(300, 512, 256, in_dtype=I.F8E4M3, act="gelu_tanh", out_dtype=I.F32)
+    run_linear(2300, 8192, 256, in_dtype=I.F8E4M3, dq_row=False, residual=True, aux=True, partials=True,
+               gamma=True, seed=1)
+
+
 def test_fp8_input_optional_scales_and_generic_chain():
     run_linear(300, 264, 160, in_dtype=I.F8E4M3, dq_col=False, act="gelu_tanh", out_dtype=I.F32)
     run_linear(300, 264, 160, in_dtype=I.F8E4M3, dq_row=False, dq_col=False, residual=True, aux=True,
@@ -351,13 +369,13 @@ def test_fp8_input_optional_scales_and_generic_chain():
     run_linear(70, 144, 48, in_dtype=I.F8E4M3, dq_row=False, bias=True, rscale=True, split=2, seed=2)
 
 
-def test_fp8_input_swiglu_fp8_output():
+@pytest.mark.parametrize("M,N,K", [(300, 528, 160), (600, 512, 256)])
+def test_fp8_input_swiglu_fp8_output(M, N, K):
     """E4M3 in, SwiGLU, E4M3 out. Near zero an output code step is finer than the E4M3 MFMA's
     block-sum error, so (as for bf16 inputs, tier 2) the same kernel with an fp32 output gives
     the pre-quantisation values: those are checked against the oracle under the accumulation
     bound carried through SwiGLU to first order, the scales must be exactly fl32(max|y32| / 448)
     and the codes within 1 ulp of y32 / s."""
-    M, N, K = 300, 528, 160
     out = run_linear(M, N, K, in_dtype=I.F8E4M3, act="swiglu", quant=True, check=False)
     y32 = host64(run_linear(M, N, K, in_dtype=I.F8E4M3, act="swiglu", out_dtype=I.F32, check=False)["y"].view)
     sa = host64(out["keep"]["sa"])
