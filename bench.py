@@ -61,17 +61,31 @@ NEXT = [
 ]
 
 
-def time_workload(run, steps: int, warmup: int) -> float:
-    """Average launch time in ms over `steps` launches after `warmup` untimed ones."""
+SETTLE_MS = 100.0
+
+
+def time_workload(run, steps: int, warmup: int, settle_ms: float = SETTLE_MS) -> float:
+    """Average launch time in ms over `steps` launches after an untimed warm-up of at least
+    `warmup` launches and at least `settle_ms` of launches. The GPU idles while a workload's
+    inputs are made on the host, and after an idle spell its clock takes a few tens of ms of
+    load to settle (measured: the first 50 ms of MLP-up launches run up to 25 % slower, the
+    first 20 ms of QKV launches up to 3x on the first one); the timed launches are the steady
+    state a loop of such layers runs in."""
     import torch
-    for i in range(warmup):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or (time.perf_counter() - t0) * 1e3 < settle_ms:
         run.launch(i)
+        i += 1
+        if i % 4 == 0:
+            torch.cuda.synchronize()    # the wall clock follows the GPU, not the enqueueing
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()                      # torch's current stream: the stream the binding launches on
-    for i in range(steps):
-        run.launch(i)
+    for j in range(steps):
+        run.launch(i + j)
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
