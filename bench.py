@@ -248,7 +248,8 @@ def main() -> int:
     ln = results.get("ln_gelu_f16_32768x4096")
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "warmup_min_ms": SETTLE_MS,
+        "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "fused-linear hot path suite (one pass of every workload at full size)",
                    "workloads": [n for n in names if n in suite]},
