@@ -141,6 +141,8 @@ def op(kind: int, tensor=None, *, out=None, split=None, head_dim=None) -> Op:
             o.out_v[i] = s.data_ptr()
     if head_dim is not None:
         o.n_split = head_dim
+    # the op holds raw device pointers: keep their tensors alive as long as the op
+    o.tensors = tuple(t for t in (tensor, out, *(split or ())) if t is not None)
     return o
 
 
@@ -202,7 +204,8 @@ def prepare_linear_epilogue(x, w, y, *, bias=None, ops=(), workspace=None, out_d
     def call() -> int:
         return fn(*args)
 
-    call.keep = (x, w, y, bias, workspace, arr)  # the buffers and the op array live as long as call
+    # the buffers, the ops (which hold their own tensors) and the op array live as long as call
+    call.keep = (x, w, y, bias, workspace, tuple(ops), arr)
     return call
 
 
@@ -234,6 +237,7 @@ def xent_op(labels, stats, target) -> Op:
     o.out = stats.data_ptr()
     o.ld = _ld(stats)
     o.out_v[0] = target.data_ptr()
+    o.tensors = (labels, stats, target)
     return o
 
 

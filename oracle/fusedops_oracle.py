@@ -42,7 +42,8 @@ from __future__ import annotations
 import math
 
 import numpy as np
-from scipy.special import erf as _erf
+from scipy.special import erfc as _erfc
+from scipy.special import expit as _expit
 
 __all__ = [
     "PARTIAL_COLS", "E4M3_MAX",
@@ -99,21 +100,26 @@ def gelu_erf(h: np.ndarray) -> np.ndarray:
     """GELU, erf form: 0.5 h (1 + erf(h / sqrt 2)) = h * Phi(h).
 
     [Fusion] §GELU激活融合 (the kernel line that applies erf to acc/sqrt 2) and
-    the Python demo's epilogue.
+    the Python demo's epilogue. Written with 1 + erf(x) = erfc(-x), the same
+    function: for h << 0 the sum 1 + erf(h / sqrt 2) cancels in float64 (at
+    h = -8 it keeps about one correct digit) while erfc keeps full relative
+    accuracy in the negative tail.
     """
     h = np.asarray(h, dtype=np.float64)
-    return 0.5 * h * (1.0 + _erf(h * _SQRT_HALF))
+    return 0.5 * h * _erfc(-h * _SQRT_HALF)
 
 
 def gelu_tanh(h: np.ndarray) -> np.ndarray:
-    """GELU, tanh form: 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))).
+    """GELU, tanh form: 0.5 h (1 + tanh(u)), u = sqrt(2/pi) (h + 0.044715 h^3).
 
     [Fusion] §GELU激活融合, the GELU(x) approximation equation; [LN+GELU]
-    §用Triton手写融合内核 (the ``inner`` / ``gelu_out`` lines).
+    §用Triton手写融合内核 (the ``inner`` / ``gelu_out`` lines). Evaluated as
+    h / (1 + e^(-2u)), the same function (1 + tanh u = 2 / (1 + e^(-2u))), so
+    that the negative tail does not cancel in 1 + tanh u.
     """
     h = np.asarray(h, dtype=np.float64)
     inner = _SQRT_2_OVER_PI * (h + _GELU_CUBIC * h * h * h)
-    return 0.5 * h * (1.0 + np.tanh(inner))
+    return h * _expit(2.0 * inner)
 
 
 def silu(g: np.ndarray) -> np.ndarray:

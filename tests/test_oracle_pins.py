@@ -38,12 +38,18 @@ def bf_contract(x, w):
 
 
 def bf_gelu_erf(v):
-    return 0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0)))
+    # 1 + erf(x) = erfc(-x): no cancellation in the negative tail
+    return 0.5 * v * math.erfc(-v / math.sqrt(2.0))
 
 
 def bf_gelu_tanh(v):
     c = math.sqrt(2.0 / math.pi)
-    return 0.5 * v * (1.0 + math.tanh(c * (v + 0.044715 * v ** 3)))
+    u = c * (v + 0.044715 * v ** 3)
+    if u >= 0.0:
+        return 0.5 * v * (1.0 + math.tanh(u))
+    # u < 0: 1 + tanh u = 2 e^(2u) / (1 + e^(2u)), which does not cancel as 1 + tanh u does
+    e = math.exp(2.0 * u)
+    return v * e / (1.0 + e)
 
 
 def bf_silu(g):
@@ -100,9 +106,9 @@ def test_zero_input_gives_activation_of_bias():
 # GELU (both forms) and SiLU
 # ---------------------------------------------------------------------------
 
-def _load_cdf():
+def _load_cdf(name="normal_cdf.txt"):
     rows = []
-    with open(os.path.join(GOLDEN, "normal_cdf.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.strip()
             if line and not line.startswith("#"):
@@ -304,6 +310,18 @@ def test_gelu_erf_textbook_normal_cdf():
     assert O.gelu_erf(np.array([-1.0]))[0] == pytest.approx(-0.15865525393145707, rel=1e-14)
 
 
+def test_gelu_erf_negative_tail_textbook():
+    # GELU_erf(-x) = -x Q(x) with Q the textbook upper tail of the normal distribution: the
+    # oracle keeps full relative accuracy down to GELU(-8) ~ -5e-15
+    for x, q in _load_cdf("normal_tail.txt"):
+        assert O.gelu_erf(np.array([-x]))[0] == pytest.approx(-x * q, rel=1e-12)
+        assert bf_gelu_erf(-x) == pytest.approx(-x * q, rel=1e-12)
+    # the tanh form in the same range against the scalar route through math.exp
+    x = np.linspace(-12.0, -3.0, 91)
+    np.testing.assert_allclose(O.gelu_tanh(x), [bf_gelu_tanh(v) for v in x], rtol=1e-12, atol=0)
+    assert (O.gelu_erf(x) < 0).all() and (O.gelu_tanh(x) < 0).all()
+
+
 @pytest.mark.parametrize("f", [O.gelu_erf, O.gelu_tanh])
 def test_gelu_closed_forms(f):
     assert f(np.array([0.0]))[0] == 0.0
@@ -458,6 +476,28 @@ def test_finalize_closed_forms():
     np.testing.assert_allclose(O.rmsnorm_apply(r0, h), O.rmsnorm_apply(r1, 5.0 * h), rtol=1e-13)
 
 
+def test_rmsnorm_apply_with_gamma_brute_force():
+    # y[m][n] = r[m] * h[m][n] * gamma[n], written out element by element (M != N so a
+    # transposed broadcast fails), and gamma = None leaves the column factor at 1
+    rng = np.random.default_rng(24)
+    M, N = 3, 5
+    r = rng.uniform(0.5, 2.0, M)
+    h = rng.standard_normal((M, N))
+    g = rng.uniform(0.5, 1.5, N)
+    got = O.rmsnorm_apply(r, h, g)
+    for m in range(M):
+        for n in range(N):
+            assert got[m, n] == pytest.approx(r[m] * h[m][n] * g[n], rel=1e-15)
+    got1 = O.rmsnorm_apply(r, h)
+    for m in range(M):
+        for n in range(N):
+            assert got1[m, n] == pytest.approx(r[m] * h[m][n], rel=1e-15)
+    # worked example: row (3, 4) with eps 0 has r = 1/sqrt(12.5); gamma (2, 0.5)
+    r0 = O.rmsnorm_finalize(O.rowsumsq_partials(np.array([[3.0, 4.0]])), 2, 0.0)
+    y = O.rmsnorm_apply(r0, np.array([[3.0, 4.0]]), np.array([2.0, 0.5]))
+    np.testing.assert_allclose(y, [[6 / math.sqrt(12.5), 2 / math.sqrt(12.5)]], rtol=1e-15)
+
+
 # ---------------------------------------------------------------------------
 # LayerNorm + GELU
 # ---------------------------------------------------------------------------
@@ -582,6 +622,29 @@ def test_e4m3_roundtrip_midpoints_and_saturation():
     assert O.e4m3_encode(np.array([2.0 ** -9]))[0] == 0x01
     assert O.e4m3_encode(np.array([2.0 ** -11]))[0] == 0x00   # below half the smallest subnormal
     assert O.e4m3_encode(np.array([3 * 2.0 ** -11]))[0] == 0x01
+
+
+def test_e4m3_ordinal_is_the_value_line():
+    # Exhaustive over the 254 finite codes: sorting the codes by value, the ordinal rises with
+    # the value (strictly, except that +0 and -0 share ordinal 0) and value-adjacent codes are
+    # exactly one ordinal apart, so |ordinal difference| counts E4M3 steps (ulps) between codes.
+    v = O.e4m3_values()
+    codes = np.array([c for c in range(256) if not np.isnan(v[c])], dtype=np.uint8)
+    assert len(codes) == 254
+    ordn = O.e4m3_ordinal(codes)
+    assert O.e4m3_ordinal(np.array([0x00]))[0] == 0 and O.e4m3_ordinal(np.array([0x80]))[0] == 0
+    order = np.argsort(v[codes], kind="stable")
+    vals, ords = v[codes][order], ordn[order]
+    for i in range(len(vals) - 1):
+        if vals[i] == vals[i + 1]:          # the two zeros
+            assert vals[i] == 0.0 and ords[i] == ords[i + 1] == 0
+        else:
+            assert ords[i + 1] - ords[i] == 1, (vals[i], vals[i + 1])
+    # the ends of the line: -448 and 448 are 126 steps from zero on either side
+    assert O.e4m3_ordinal(np.array([0x7E, 0xFE])).tolist() == [126, -126]
+    # a distance of 1 between neighbours across zero: the smallest subnormals of either sign
+    assert O.e4m3_ordinal(np.array([0x01]))[0] - O.e4m3_ordinal(np.array([0x81]))[0] == 2
+    assert O.e4m3_ordinal(np.array([0x01]))[0] - O.e4m3_ordinal(np.array([0x80]))[0] == 1
 
 
 def test_e4m3_matches_torch_cast_in_range():
