@@ -614,16 +614,21 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     const int i = threadIdx.x, t = t0 + i;
     if (f0 == 0 && t < M) e.scales[t] = __fdiv_rn(s_amax[i], 448.0f);
   }
-  float inv[4];
+  Fp8RowFactor fac[4];
+  bool tiny = false;
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const float s = __fdiv_rn(s_amax[tk(tb)], 448.0f);  // IEEE division: s = fl32(a / 448)
-    inv[tb] = s > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+    fac[tb] = fp8_row_factor(__fdiv_rn(s_amax[tk(tb)], 448.0f));  // IEEE division: s = fl32(a / 448)
+    tiny |= fac[tb].pre != 1.f;
   }
+  // rows with a scale below 2^-100 (the pre-scaled path) are rare: a wave-uniform test keeps
+  // the extra multiply out of every other wave
+  const bool any_tiny = __ballot(tiny) != 0;
   emit(ydt, pairs, dy, [&](int fb, int tb) __attribute__((always_inline)) {
     f32x16 v = acc[fb][tb];
+    if (any_tiny) v *= fac[tb].pre;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = fminf(fmaxf(v[r] * inv[tb], -448.f), 448.f);
+    for (int r = 0; r < 16; ++r) v[r] = fminf(fmaxf(v[r] * fac[tb].inv, -448.f), 448.f);
     return v;
   });
 }

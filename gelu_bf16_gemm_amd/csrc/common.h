@@ -138,6 +138,20 @@ __device__ __forceinline__ int dtype_bytes(int dtype) {
   return dtype == FUSEDOPS_F32 ? 4 : (dtype == FUSEDOPS_F8E4M3 ? 1 : 2);
 }
 
+// Per-row factors of FP8 quantisation: q = clamp(v * pre * inv, +-448) stands for v / s. For
+// s >= 2^-100 (every row whose absmax exceeds 448 * 2^-100 ~ 3.5e-28) pre = 1 and inv =
+// fl(1 / s); for smaller s, 1 / s can overflow (s below 2^-128), so v is first scaled by the
+// power of two 2^64 (exact: v <= 448 s is tiny) and inv = fl(1 / (s 2^64)). A zero row (s = 0)
+// gets inv = 0 and all-zero codes.
+struct Fp8RowFactor {
+  float pre, inv;
+};
+__device__ __forceinline__ Fp8RowFactor fp8_row_factor(float s) {
+  if (!(s > 0.f)) return {1.f, 0.f};
+  if (s >= 0x1p-100f) return {1.f, __fdiv_rn(1.0f, s)};
+  return {0x1p64f, __fdiv_rn(1.0f, s * 0x1p64f)};
+}
+
 // ---------------------------------------------------------------------------
 // activations (fp32 in registers)
 // ---------------------------------------------------------------------------
@@ -163,6 +177,17 @@ __device__ __forceinline__ float gelu_erf_f32(float v) {
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(a, P, 1.0f));
   const float poly = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, A5, A4), A3), A2), A1);
   const float h = poly * __builtin_amdgcn_exp2f((v * E) * v);
+  return __builtin_fmaf(-a, h, fmaxf(v, 0.f));
+}
+
+// GELU, erf form, for fp32 outputs: the same v Phi(v) = max(v, 0) - |v| h with h = 0.5 erfc(|v| / sqrt 2)
+// taken from the device math library's erfcf (a few ulp of relative error over its whole range),
+// so the negative tail keeps fp32 relative accuracy (A&S 7.1.26 bounds the absolute error of erf
+// only: its relative error in h grows to 1.6e-3 at v = -5 and 1e-2 at v = -8). The rounding of
+// |v| / sqrt 2 adds a relative error of about 2 (v^2 / 2) 2^-24 to h, 4e-6 at v = -8.
+__device__ __forceinline__ float gelu_erf_precise_f32(float v) {
+  const float a = fabsf(v);
+  const float h = 0.5f * erfcf(a * 0.70710678118654752f);
   return __builtin_fmaf(-a, h, fmaxf(v, 0.f));
 }
 

@@ -219,6 +219,11 @@ __device__ __forceinline__ void rendezvous_row_amax(const EpiParams& e, int ft, 
   uint32_t gen = 0;
   if (threadIdx.x == 0) {
     gen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The flag must be read before this tile arrives: relaxed accesses to different words may
+    // be performed in either order, and a read performed after the last arrival could return
+    // the raised value (the tile would then wait for a generation that never comes). Waiting
+    // for the load's data before issuing the arrival orders them.
+    __builtin_amdgcn_s_waitcnt(0);
     uint32_t* gc = rec + 64 + 32 * g;
     const bool last = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                       (uint32_t)in_group - 1;
@@ -412,8 +417,15 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     }
     // activation; SwiGLU leaves its 4 outputs in v[0..3]
     if (e.act == ACT_GELU_ERF) {
+      // fp32 outputs keep fp32 relative accuracy in the negative tail; 16-bit and E4M3
+      // outputs take the shorter A&S form, whose error is far below their rounding
+      if (e.y_dtype == FUSEDOPS_F32) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = gelu_erf_f32(v[i]);
+        for (int i = 0; i < 8; ++i) v[i] = gelu_erf_precise_f32(v[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = gelu_erf_f32(v[i]);
+      }
     } else if (e.act == ACT_GELU_TANH) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = gelu_tanh_f32(v[i]);
@@ -496,12 +508,12 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
       if (!t_ok) continue;
       const float amax = amax_rows[r];
       const float s = __fdiv_rn(amax, 448.0f);  // IEEE division: s = fl32(a / 448)
-      const float inv = s > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+      const Fp8RowFactor fac = fp8_row_factor(s);
       if (f0 == 0 && g == 0) e.scales[t] = s;
       if (!f_ok) continue;
       float q[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(v[i] * inv, -448.f), 448.f);
+      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf((v[i] * fac.pre) * fac.inv, -448.f), 448.f);
       uint8_t* yrow = static_cast<uint8_t*>(e.y) + (int64_t)t * e.ldy;
       if (swiglu) {
         *reinterpret_cast<uint32_t*>(yrow + fo) = pack_e4m3x2(q[0], q[1]) | (pack_e4m3x2(q[2], q[3]) << 16);

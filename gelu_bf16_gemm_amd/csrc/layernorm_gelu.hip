@@ -168,7 +168,8 @@ __global__ __launch_bounds__(kThreads) void ln_gelu_kernel(LnArgs a) {
     for (int i = 0; i < EPC; ++i) {
       const float yv = (v[j][i] - mean) * rstd * g[i] + b[i];
       o[i] = a.gelu_form == FUSEDOPS_GELU_TANH ? gelu_tanh_f32(yv)
-             : a.gelu_form == FUSEDOPS_GELU_ERF ? gelu_erf_f32(yv) : yv;
+             : a.gelu_form != FUSEDOPS_GELU_ERF ? yv
+             : a.out_dtype == FUSEDOPS_F32 ? gelu_erf_precise_f32(yv) : gelu_erf_f32(yv);
     }
     store_chunk<EPC>(yrow, a.out_dtype, (int64_t)c * EPC, o);
   }
@@ -264,7 +265,8 @@ void ln_gelu_rows_kernel(LnArgs a) {
       for (int i = 0; i < EPC; ++i) {
         const float yv = (chunk_elem<EPC>(xr[j], a.io_dtype, i) - mean) * rstd * g[i] + b[i];
         o[i] = a.gelu_form == FUSEDOPS_GELU_TANH ? gelu_tanh_f32(yv)
-               : a.gelu_form == FUSEDOPS_GELU_ERF ? gelu_erf_f32(yv) : yv;
+               : a.gelu_form != FUSEDOPS_GELU_ERF ? yv
+               : a.out_dtype == FUSEDOPS_F32 ? gelu_erf_precise_f32(yv) : gelu_erf_f32(yv);
       }
       store_chunk<EPC>(yrow, a.out_dtype, (int64_t)c * EPC, o);
     }

@@ -1,14 +1,5 @@
-"""Test-side helpers: device upload of stored inputs, guard-banded outputs and the
-comparison rules (tolerances stated once, here).
-
-Tolerances (per output kind):
-* bf16 / fp16:  |y - ref| <= 2e-2 + 2e-2 |ref|, element by element.
-* fp32:         |y - ref| <= 1e-4 * max(|ref|, rho), rho = RMS of the reference tensor.
-  "1e-4 relative" needs a floor where the reference crosses zero (GELU at 0), where fp32
-  accumulation error does not vanish; the RMS floor never binds for positive outputs
-  such as row partials and RMSNorm scales.
-* E4M3 codes:   with the GPU's own row scale s, q_ref = E4M3_RNE(clamp(v_ref / s, +-448));
-  the ordinal distance between q_gpu and q_ref is at most 1 (+0 and -0 coincide).
+"""Test-side helpers: device upload of stored inputs and guard-banded outputs. The comparison
+rules (tolerances, stated once) live in oracle/parity.py and are re-exported here.
 """
 
 from __future__ import annotations
@@ -18,8 +9,10 @@ import sys
 import numpy as np
 import torch
 
-import oracle as O
+import oracle as O  # noqa: F401
 from gelu_bf16_gemm_amd import inputs as I
+from oracle.parity import (F32_TINY, U32, check_f32, check_f32_e4m3_acc, check_fp8, check_lowp,  # noqa: F401
+                           check_out, gemm_floor)
 
 TORCH_DT = {I.F32: torch.float32, I.BF16: torch.bfloat16, I.F16: torch.float16, I.F8E4M3: torch.uint8}
 SENTINEL = 0x5A
@@ -65,62 +58,6 @@ class Guarded:
         mask = np.ones(full.shape, dtype=bool)
         mask[self.g:self.g + self.rows, :self.cols * es] = False
         return bool((full[mask] == SENTINEL).all())
-
-
-def check_lowp(y: np.ndarray, ref: np.ndarray, what: str) -> None:
-    y = np.asarray(y, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert y.shape == ref.shape, (what, y.shape, ref.shape)
-    assert np.isfinite(y).all(), f"{what}: non-finite output"
-    err = np.abs(y - ref)
-    bound = 2e-2 + 2e-2 * np.abs(ref)
-    bad = err > bound
-    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside 2e-2+2e-2|ref|; "
-                           f"worst err {err.max():.3g} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
-
-
-def check_f32(y: np.ndarray, ref: np.ndarray, what: str, rel: float = 1e-4) -> None:
-    y = np.asarray(y, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert y.shape == ref.shape, (what, y.shape, ref.shape)
-    assert np.isfinite(y).all(), f"{what}: non-finite output"
-    rho = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    bound = rel * np.maximum(np.abs(ref), rho)
-    err = np.abs(y - ref)
-    bad = err > bound
-    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside {rel}*max(|ref|, rms); "
-                           f"worst rel {(err / np.maximum(np.abs(ref), rho)).max():.3g}")
-
-
-def check_f32_e4m3_acc(y: np.ndarray, ref: np.ndarray, mag: np.ndarray, what: str) -> None:
-    """fp32 outputs of E4M3 inputs. The E4M3 MFMA sums each block of 64 products with its own
-    internal alignment rather than exact fp32 additions (an in-bounds probe of one instruction
-    measured errors up to 2.1e-4 of the block's sum of |products| on random codes, exact sums
-    when the terms align), so the bound scales with mag = sum_k |x_k w_k| |sa sw| and an
-    epilogue amplification of at most 2: 1e-3 * mag + 1e-4 * max(|ref|, rms)."""
-    y = np.asarray(y, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert y.shape == ref.shape, (what, y.shape, ref.shape)
-    assert np.isfinite(y).all(), f"{what}: non-finite output"
-    rho = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    bound = 1e-3 * mag + 1e-4 * np.maximum(np.abs(ref), rho)
-    err = np.abs(y - ref)
-    bad = err > bound
-    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside 1e-3 mag + 1e-4 max(|ref|, rms)"
-
-
-def check_out(y: np.ndarray, ref: np.ndarray, dtype: int, what: str) -> None:
-    if dtype == I.F32:
-        check_f32(y, ref, what)
-    else:
-        check_lowp(y, ref, what)
-
-
-def check_fp8(codes: np.ndarray, scales: np.ndarray, vref: np.ndarray, what: str) -> None:
-    codes = np.asarray(codes, np.uint8)
-    q_ref = O.quantize_fp8_rows(vref, scales)
-    d = np.abs(O.e4m3_ordinal(codes) - O.e4m3_ordinal(q_ref))
-    assert (d <= 1).all(), f"{what}: {int((d > 1).sum())} codes more than 1 ulp away (max {d.max()})"
 
 
 def workspace_ok(ws) -> bool:

@@ -15,7 +15,7 @@ import oracle as O
 from gelu_bf16_gemm_amd import inputs as I
 
 from helpers import (workspace_ok, Guarded, check_f32, check_f32_e4m3_acc, check_fp8, check_lowp, check_out, dev,
-                     host64, note)
+                     gemm_floor, host64, note)
 
 pytestmark = pytest.mark.gpu
 
@@ -136,7 +136,29 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
                             row_scale=None if r is None else r.astype(np.float64), act=act)
     if cs is not None:
         ref["y"] = O.rope_pairs(ref["y"], cs.astype(np.float64), rope, N - N // split if split else N)
-    out = {"ref": ref, "keep": keep, "y": y, "ws": ws, "X": X, "W": W}
+    # fp32 error floors (16-bit outputs ignore them): the accumulation bound of each
+    # pre-activation carried through gamma, r, the activation and RoPE
+    mag = np.abs(xv) @ np.abs(wv).T
+    if sa is not None:
+        mag = mag * sa.astype(np.float64)[:, None]
+    if sw is not None:
+        mag = mag * sw.astype(np.float64)[None, :]
+    if b is not None:
+        mag = mag + np.abs(I.to_f64(b, vec_dt))[None, :]
+    if z is not None:
+        mag = mag + np.abs(I.to_f64(z, zdt))
+    scale = np.ones((M, N))
+    if g is not None:
+        scale = scale * np.abs(I.to_f64(g, zdt))[None, :]
+    if r is not None:
+        scale = scale * r.astype(np.float64)[:, None]
+    pre = ref["h1"] * (1.0 if g is None else I.to_f64(g, zdt)[None, :]) * (1.0 if r is None else r.astype(np.float64)[:, None])
+    floor_y = gemm_floor(K, mag, pre, act, scale)
+    if cs is not None:  # a rotated pair mixes both members' errors
+        pair = floor_y[:, 0::2] + floor_y[:, 1::2]
+        floor_y = np.repeat(pair, 2, axis=1)
+    floor_h1 = gemm_floor(K, mag, ref["h1"])
+    out = {"ref": ref, "keep": keep, "y": y, "ws": ws, "X": X, "W": W, "floor_y": floor_y}
     if not check:
         return out
     if y is not None:
@@ -154,7 +176,8 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
         d = N // split
         for i, sg in enumerate(keep["split"]):
             assert sg.intact()
-            check_out(host64(sg.view), ref["y"][:, i * d:(i + 1) * d], out_dtype, f"split block {i}")
+            check_out(host64(sg.view), ref["y"][:, i * d:(i + 1) * d], out_dtype, f"split block {i}",
+                      floor_y[:, i * d:(i + 1) * d])
     elif fp8 and out_dtype == I.F32:
         mag = np.abs(xv) @ np.abs(wv).T
         if sa is not None:
@@ -164,14 +187,16 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
         assert act != "swiglu"
         check_f32_e4m3_acc(host64(y.view), ref["y"], 2.0 * mag, "Y")
     else:
-        check_out(host64(y.view), ref["y"], out_dtype, "Y")
+        check_out(host64(y.view), ref["y"], out_dtype, "Y", floor_y)
     if aux:
         adt = aux_dtype if aux_dtype is not None else zdt
         assert keep["aux"].intact()
-        check_out(host64(keep["aux"].view), ref["h1"], adt, "aux h1")
+        check_out(host64(keep["aux"].view), ref["h1"], adt, "aux h1", floor_h1)
     if partials:
         assert keep["p"].intact()
-        check_f32(host64(keep["p"].view), ref["partials"], "row partials")
+        T = -(-N // 128)
+        floor_p = np.stack([(2 * np.abs(ref["h1"]) * floor_h1)[:, 128 * t:128 * (t + 1)].sum(1) for t in range(T)], 1)
+        check_f32(host64(keep["p"].view), ref["partials"], "row partials", floor_p)
     return out
 
 
@@ -254,7 +279,8 @@ def test_qkv_split_scaled_blocks_bit_exact():
     q, k, v = (host64(o.view) for o in outs)
     assert np.array_equal(k, 2 * q) and np.array_equal(v, 4 * q)
     ref = O.linear_epilogue(I.to_f64(X, I.BF16), I.to_f64(W, I.BF16), bias=I.to_f64(b, I.BF16))["y"]
-    check_f32(np.hstack([q, k, v]), ref, "qkv f32")
+    mag = np.abs(I.to_f64(X, I.BF16)) @ np.abs(I.to_f64(W, I.BF16)).T + np.abs(I.to_f64(b, I.BF16))[None, :]
+    check_f32(np.hstack([q, k, v]), ref, "qkv f32", gemm_floor(K, mag, ref))
 
 
 # (2300, 8192, 128) and (2300, 8200, 136): more 256 x 256 tiles than the device holds at once,
@@ -266,9 +292,9 @@ def test_swiglu_fp8_rows(M, N, K):
     out = run_linear(M, N, K, act="swiglu", quant=True)
     # tier 2: the same kernel with an fp32 output gives the pre-quantisation values;
     # the scale must be exactly fl32(max|y32| / 448) and the codes within 1 ulp of them
-    y32 = run_linear(M, N, K, act="swiglu", out_dtype=I.F32, seed=0, check=False)["y"]
-    y32 = host64(y32.view)
-    check_f32(y32, out["ref"]["y"], "pre-quantisation values")
+    r32 = run_linear(M, N, K, act="swiglu", out_dtype=I.F32, seed=0, check=False)
+    y32 = host64(r32["y"].view)
+    check_f32(y32, out["ref"]["y"], "pre-quantisation values", r32["floor_y"])
     s = host64(out["keep"]["s"].view[0]).astype(np.float32)
     a_gpu = np.abs(y32).max(axis=1).astype(np.float32)
     assert np.array_equal(s, O.fp8_row_scale(a_gpu)), "scale is not fl32(absmax / 448)"
@@ -466,6 +492,70 @@ def test_fp8_tier1_exact_scales_and_codes():
     assert workspace_ok(ws)
 
 
+def _tiny_scale_rows(M, K, rng, exps):
+    """Tier-1 rows: E4M3 values and midpoints q times 2^-E with one element at +-448 2^-E, E
+    cycling over `exps`. Codes below 2^(E - 126) are left out so every element stays a normal
+    fp32 number (subnormal inputs are not what is tested here)."""
+    vals = O.e4m3_values()[:0x7F]
+    pool0 = np.concatenate([vals, (vals[:-1] + vals[1:]) / 2])
+    X32 = np.zeros((M, K), np.float32)
+    for m in range(M):
+        E = exps[m % len(exps)]
+        pool = pool0[pool0 >= 2.0 ** max(0, E - 126)]
+        row = rng.choice(np.concatenate([pool, -pool]), size=K)
+        row[rng.integers(K)] = 448.0 if m % 2 == 0 else -448.0
+        X32[m] = (row * 2.0 ** -E).astype(np.float32)
+    assert np.isfinite(X32).all() and (np.abs(X32[X32 != 0]) >= np.finfo(np.float32).tiny).all()
+    return X32
+
+
+@pytest.mark.parametrize("in_dtype,M,swiglu", [(I.BF16, 40, False), (I.BF16, 300, False), (I.BF16, 300, True),
+                                               (I.F32, 40, False)])
+def test_fp8_tiny_row_scales(in_dtype, M, swiglu):
+    """Rows whose absmax is near 1e-36: s = fl32(a / 448) is 2^-110, 2^-127 (subnormal) or
+    2^-128 / 2^-129 (subnormal, no finite fp32 reciprocal); the codes must still be
+    E4M3_RNE(v / s) and the scales bit-exact (tier 1: every value exact in fp32)."""
+    K = 64
+    rng = np.random.default_rng(81)
+    if swiglu:
+        # y_j = silu(64) x_j = 64 x_j: 1 + e^-64 rounds to 1 in fp32, so silu(64) is exactly 64
+        # there; s = 64 * 2^-E = 2^(6 - E)
+        X32 = _tiny_scale_rows(M, K, rng, [6, 116, 133, 134])
+        Kx = K + 16                                       # x then the constant-64 gate column, K % 16 == 0
+        Xf = np.zeros((M, Kx), np.float32)
+        Xf[:, :K] = X32
+        Xf[:, K] = 64.0
+        Wf = np.zeros((2 * K, Kx), np.float32)
+        Wf[0::2, K] = 1.0                                 # gate rows pick the constant column
+        Wf[1::2, :K] = np.eye(K, dtype=np.float32)        # up rows pick x_j
+        N, vref, ops_act = 2 * K, 64.0 * X32.astype(np.float64), [B.op(B.OP_SWIGLU)]
+    else:
+        X32 = _tiny_scale_rows(M, K, rng, [0, 110, 127, 129])
+        Xf, Wf, Kx, N, vref, ops_act = X32, np.eye(K, dtype=np.float32), K, K, X32.astype(np.float64), []
+    X = I.store(Xf, in_dtype)
+    W = I.store(Wf, in_dtype)
+    assert np.array_equal(I.to_f64(X, in_dtype), Xf.astype(np.float64))
+    n_out = N // 2 if swiglu else N
+    y = Guarded(M, n_out, I.F8E4M3)
+    s = torch.full((M,), -1.0, dtype=torch.float32, device="cuda")
+    ops = ops_act + [B.op(B.OP_QUANT_FP8_ROW, out=s)]
+    ws = torch.zeros(B.fusedops_linear_workspace_bytes(M, N, Kx, ops) // 4, dtype=torch.int32, device="cuda")
+    note(f"fp8 tiny row scales in={in_dtype} M={M} swiglu={swiglu}")
+    assert B.fusedops_linear_epilogue(dev(X, in_dtype), dev(W, in_dtype), y.view, ops=ops, workspace=ws,
+                                      out_dtype=I.F8E4M3) == B.OK
+    torch.cuda.synchronize()
+    s_ref = O.fp8_row_scale(np.abs(vref).max(1))
+    assert (s_ref[2::4] < 2.0 ** -100).all() and (s_ref[3::4] <= 2.0 ** -128).all()
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(1.0) / s_ref[3::4]).all()   # no finite fp32 reciprocal
+    assert np.array_equal(host64(s).astype(np.float32), s_ref)
+    q_ref = O.quantize_fp8_rows(vref, s_ref)
+    got = host64(y.view)
+    bad = np.argwhere(O.e4m3_ordinal(got) != O.e4m3_ordinal(q_ref))
+    assert bad.size == 0, f"{len(bad)} codes differ, rows {sorted(set(bad[:, 0].tolist()))[:10]}"
+    assert y.intact() and workspace_ok(ws)
+
+
 @pytest.mark.parametrize("M,N,K", [(40, 4160, 64), (300, 1056, 136), (2300, 8192, 128)])
 def test_fp8_workspace_reused_across_calls(M, N, K):
     """One workspace, several quantised calls in a row on different inputs (the release
@@ -530,8 +620,38 @@ def test_fp32_linear_gelu_full_size():
                                     bias=dev(inp["b"], I.F32), ops=[B.op(B.OP_GELU_ERF)])
     assert st == B.OK
     torch.cuda.synchronize()
-    ref = O.linear_epilogue(inp["X"], inp["W"], bias=inp["b"], act="gelu_erf")["y"]
-    check_f32(host64(y.view), ref, "fp32 Y")
+    ref = O.linear_epilogue(inp["X"], inp["W"], bias=inp["b"], act="gelu_erf")
+    mag = np.abs(inp["X"].astype(np.float64)) @ np.abs(inp["W"].astype(np.float64)).T + np.abs(inp["b"])[None, :]
+    check_f32(host64(y.view), ref["y"], "fp32 Y", gemm_floor(256, mag, ref["h1"], "gelu_erf"))
+    assert y.intact()
+
+
+@pytest.mark.parametrize("in_dtype,M,N,K", [(I.F32, 64, 256, 256), (I.F32, 100, 200, 600), (I.BF16, 300, 264, 136),
+                                             (I.BF16, 40, 256, 256)])
+def test_gelu_erf_negative_tail_fp32_output(in_dtype, M, N, K):
+    """fp32 outputs whose pre-activations lie in [-8, -3], where GELU_erf is v Phi(v) with Phi
+    between 6e-16 and 1.3e-3: the output must hold 1e-4 relative accuracy there (the
+    accumulation floor vanishes with the slope of GELU)."""
+    rng = np.random.default_rng([404, M, N, K, in_dtype])
+    X = I.random_stored(rng, (M, K), in_dtype)
+    W = I.random_stored(rng, (N, K), in_dtype, std=1 / math.sqrt(K))
+    b = I.store(rng.uniform(-7.0, -4.0, N).astype(np.float32), in_dtype)
+    xv, wv, bv = I.to_f64(X, in_dtype), I.to_f64(W, in_dtype), I.to_f64(b, in_dtype)
+    y = Guarded(M, N, I.F32)
+    note(f"gelu erf negative tail in={in_dtype} M={M} N={N} K={K}")
+    st = B.fusedops_linear_epilogue(dev(X, in_dtype), dev(W, in_dtype), y.view, bias=dev(b, in_dtype),
+                                    ops=[B.op(B.OP_GELU_ERF)], out_dtype=I.F32)
+    assert st == B.OK, B.status_string(st)
+    torch.cuda.synchronize()
+    ref = O.linear_epilogue(xv, wv, bias=bv, act="gelu_erf")
+    pre = ref["h1"]
+    assert ((pre > -8.5) & (pre < -2.5)).mean() > 0.95
+    mag = np.abs(xv) @ np.abs(wv).T + np.abs(bv)[None, :]
+    got = host64(y.view)
+    check_f32(got, ref["y"], "GELU_erf tail", gemm_floor(K, mag, pre, "gelu_erf"))
+    tail = (pre > -8) & (pre < -3)
+    rel = np.abs(got[tail] - ref["y"][tail]) / np.abs(ref["y"][tail])
+    assert np.median(rel) < 1e-5, np.median(rel)
     assert y.intact()
 
 
@@ -602,7 +722,10 @@ def run_pattern_a(M, d, K0, N2, *, act="swiglu", out_dtype=I.BF16, eps=1e-6, see
     check_out(host64(h1.view), ref["h1"], I.BF16, "h1")
     check_f32(host64(p.view), ref["partials"], "partials")
     check_out(host64(h2), ref["h2"], I.BF16, "h2")
-    check_out(host64(y.view), ref["y"], out_dtype, "y")
+    h2v, w1v = host64(h2), I.to_f64(W1, I.BF16)
+    pre = ref["r"][:, None] * (h2v @ w1v.T)
+    floor = gemm_floor(d, np.abs(h2v) @ np.abs(w1v).T, pre, act, ref["r"][:, None])
+    check_out(host64(y.view), ref["y"], out_dtype, "y", floor)
     return {"h2": h2, "p": p, "y": y, "W1": W1}
 
 
@@ -669,16 +792,34 @@ def run_xent(M, N, K, *, store_logits=False, bias=False, act=None, in_dtype=I.BF
                             w_scale=None if sw is None else sw.astype(np.float64))["y"]
     m_ref, s_ref = O.xent_chunk_stats(ref, B.XENT_COLS)
     got = host64(stats.view)
-    check = check_f32 if in_dtype != I.F8E4M3 else (lambda g, r, w: check_lowp(g, r, w))
-    check(got[:, 0::2], m_ref, "chunk max")
-    check(got[:, 1::2], s_ref, "chunk sum-exp")
+    # error of each logit: the fp32 accumulation floor (bf16 inputs) or the E4M3 block-sum bound
+    # (1e-3 sum_k |x_k w_k| sa sw, see check_f32_e4m3_acc), through the activation
+    mag = np.abs(xv) @ np.abs(wv).T
+    if sa is not None:
+        mag = mag * sa.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
+    pre = O.linear_epilogue(xv, wv, bias=None if b is None else I.to_f64(b, I.BF16),
+                            x_scale=None if sa is None else sa.astype(np.float64),
+                            w_scale=None if sw is None else sw.astype(np.float64))["y"]
+    if b is not None:
+        mag = mag + np.abs(I.to_f64(b, I.BF16))[None, :]
+    if in_dtype == I.F8E4M3:
+        assert act is None
+        dy = 1e-3 * mag
+    else:
+        dy = gemm_floor(K, mag, pre, act)
+    # per chunk: the maximum moves by at most the largest logit error, sum e^(y - m) by a factor
+    # e^(+-2 max error); the loss by at most 4 times the row's largest logit error
+    dchunk = np.stack([dy[:, 64 * t:64 * (t + 1)].max(1) for t in range(T)], 1)
+    check_f32(got[:, 0::2], m_ref, "chunk max", dchunk)
+    check_f32(got[:, 1::2], s_ref, "chunk sum-exp", s_ref * np.expm1(2 * dchunk))
     valid = (labels >= 0) & (labels < N)
     t_gpu = host64(tgt.view[0])
-    check(t_gpu[valid], ref[np.arange(M), np.clip(labels, 0, N - 1)][valid], "target logits")
+    lab_c = np.clip(labels, 0, N - 1)
+    check_f32(t_gpu[valid], ref[np.arange(M), lab_c][valid], "target logits", dy[np.arange(M), lab_c][valid])
     sentinel = host64(Guarded(1, 1, I.F32).view[0])[0]
     assert np.all(t_gpu[~valid] == sentinel), "target written for an ignored row"
     l_ref = O.cross_entropy(ref, labels)
-    check(host64(loss.view[0]), l_ref, "loss")
+    check_f32(host64(loss.view[0]), l_ref, "loss", 4 * dy.max(1))
     if y is not None:
         check_lowp(host64(y.view), ref, "logits")
 
