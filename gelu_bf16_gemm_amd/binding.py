@@ -44,7 +44,7 @@ LN_MAX_COLS = 16384
 # every symbol the public header declares
 EXPORTS = ("fusedops_linear_epilogue", "fusedops_linear_workspace_bytes", "fusedops_layernorm_gelu",
            "fusedops_rmsnorm_finalize", "fusedops_cross_entropy_finalize", "fusedops_partial_cols",
-           "fusedops_abi_version", "fusedops_status_string")
+           "fusedops_abi_version", "fusedops_status_string", "fusedops_rendezvous_error")
 
 
 class Op(ctypes.Structure):
@@ -71,6 +71,8 @@ lib.fusedops_rmsnorm_finalize.argtypes = [_vp, _i64, _i64, _i64, _i64, _f32, _vp
                                           _vp, _i64, _i32, _vp]
 lib.fusedops_cross_entropy_finalize.restype = _i32
 lib.fusedops_cross_entropy_finalize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
+lib.fusedops_rendezvous_error.restype = _i32
+lib.fusedops_rendezvous_error.argtypes = [_vp, _i32, ctypes.POINTER(_i32), _vp]
 lib.fusedops_partial_cols.restype = _i32
 lib.fusedops_partial_cols.argtypes = []
 lib.fusedops_abi_version.restype = _i32
@@ -245,6 +247,13 @@ def fusedops_cross_entropy_finalize(stats, n_cols: int, target, labels, loss, *,
     M = stats.shape[0]
     return lib.fusedops_cross_entropy_finalize(stats.data_ptr(), _ld(stats), M, n_cols, target.data_ptr(),
                                                labels.data_ptr(), loss.data_ptr(), _stream(stream))
+
+
+def fusedops_rendezvous_error(workspace, *, clear: bool = False, stream=None) -> tuple:
+    """(status, error word 0 / 1) of an FP8 workspace; synchronises the stream."""
+    err = _i32(-1)
+    st = lib.fusedops_rendezvous_error(_ptr(workspace), 1 if clear else 0, ctypes.byref(err), _stream(stream))
+    return st, err.value
 
 
 def abi_version() -> int:

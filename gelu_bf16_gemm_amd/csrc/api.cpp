@@ -395,6 +395,24 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   }
 }
 
+int32_t fusedops_rendezvous_error(void* workspace, int32_t clear, int32_t* error, void* stream) {
+  if (!workspace || !error) return FUSEDOPS_ERR_INVALID_ARG;
+  if (!aligned(workspace, 16)) return FUSEDOPS_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return launch_status(hipErrorInvalidValue, "rendezvous error read");
+  if (clear && word != 0) {
+    const uint32_t zero = 0;
+    if (hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return launch_status(hipErrorInvalidValue, "rendezvous error clear");
+  }
+  *error = word != 0 ? 1 : 0;
+  return FUSEDOPS_OK;
+}
+
 int32_t fusedops_layernorm_gelu(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows,
                                 int64_t cols, int32_t io_dtype, int32_t out_dtype, const void* gamma,
                                 const void* beta, int32_t param_dtype, float eps, int32_t gelu_form,

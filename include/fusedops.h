@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define FUSEDOPS_ABI_VERSION 3
+#define FUSEDOPS_ABI_VERSION 4
 /* Width of one RMSNorm row partial: p[m,t] covers columns [128 t, 128 t + 128). */
 #define FUSEDOPS_PARTIAL_COLS 128
 /* Column width of the cross-entropy chunk statistics (XENT). */
@@ -193,8 +193,8 @@ typedef struct fusedops_op {
  *          it (say decode and prefill of one layer); calls with different N need workspaces of
  *          their own. Its first 32-bit word is an error word the kernels set to 1 if a row
  *          rendezvous ever gave up waiting (the quantised output of that call is then
- *          unreliable); the library never clears it. Calls that may run concurrently
- *          (different streams) must not share a workspace.
+ *          unreliable); fusedops_rendezvous_error reads and clears it, the kernels never clear
+ *          it. Calls that may run concurrently (different streams) must not share a workspace.
  *   stream hipStream_t.
  * Outputs are written in fp32 -> out dtype with round-to-nearest-even.
  * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE, LAUNCH (see enum).
@@ -209,6 +209,25 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
  * the call itself then reports the error. */
 size_t fusedops_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, const fusedops_op* ops,
                                        int32_t n_ops);
+
+/*
+ * fusedops_rendezvous_error — whether an FP8 row rendezvous gave up waiting.
+ *
+ * A QUANT_FP8_ROW call merges each row's absmax across the column tiles of the row inside the
+ * kernel ([Epilogue] §仿射量化与尾声的五步, step 1: per-tile maxima merged over the whole row);
+ * a tile waits for the other tiles of its rows with a bounded wait, and on a timeout the kernel
+ * still finishes but sets the workspace's error word. Kernel faults cannot be returned by the
+ * asynchronous call itself, so this query reports them.
+ *
+ *   workspace  a workspace passed to fusedops_linear_epilogue (device pointer, 16-byte aligned).
+ *   clear      non-zero: reset the error word to 0 after reading it.
+ *   error      host output: 0 if every rendezvous since the word was last cleared completed,
+ *              1 if one gave up (the quantised output of that call is unreliable).
+ *   stream     synchronised before the word is read (the query waits for the calls on it).
+ * Allocates nothing. Errors: INVALID_ARG (null workspace or error), MISALIGNED, LAUNCH (a HIP
+ * copy or synchronisation failed; *error is then untouched).
+ */
+int32_t fusedops_rendezvous_error(void* workspace, int32_t clear, int32_t* error, void* stream);
 
 /*
  * fusedops_layernorm_gelu — y = GELU(LayerNorm(x) * gamma + beta) per row.

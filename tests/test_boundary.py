@@ -32,14 +32,14 @@ def test_header_symbols_are_exported():
 
 
 def test_constants():
-    assert B.abi_version() == 3
+    assert B.abi_version() == 4
     assert B.partial_cols() == 128
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
     assert B.status_string(0) == "ok"
     text = open(HEADER).read()
     assert "#define FUSEDOPS_PARTIAL_COLS 128" in text
-    assert "#define FUSEDOPS_ABI_VERSION 3" in text
+    assert "#define FUSEDOPS_ABI_VERSION 4" in text
 
 
 def lin(X=addr(0), ldx=64, W=addr(1), ldw=64, bias=None, M=32, N=64, K=64, in_dt=B.BF16, ops=(),
@@ -250,6 +250,14 @@ def test_quant_workspace_limit():
     # a quarter of the tokens fits
     need_q = B.fusedops_linear_workspace_bytes(M // 4, N, K, [sw, q])
     assert 0 < need_q < (1 << 32)
+
+
+def test_rendezvous_error_rules():
+    err = ctypes.c_int32(7)
+    assert B.lib.fusedops_rendezvous_error(None, 0, ctypes.byref(err), None) == B.ERR_INVALID_ARG
+    assert B.lib.fusedops_rendezvous_error(addr(7), 0, None, None) == B.ERR_INVALID_ARG
+    assert B.lib.fusedops_rendezvous_error(addr(7, 4), 0, ctypes.byref(err), None) == B.ERR_MISALIGNED
+    assert err.value == 7   # untouched on an argument error
 
 
 def test_aliasing_rules():

@@ -556,6 +556,19 @@ def test_fp8_tiny_row_scales(in_dtype, M, swiglu):
     assert y.intact() and workspace_ok(ws)
 
 
+def test_rendezvous_error_query():
+    """The error word through the API: 0 after a completed quantised call; a word set from the
+    host (standing in for a rendezvous that gave up: no kernel is made to time out) reads as 1,
+    and clearing resets it."""
+    out = run_linear(300, 528, 136, act="swiglu", quant=True)
+    ws = out["ws"]
+    assert B.fusedops_rendezvous_error(ws) == (B.OK, 0)
+    ws[0] = 1
+    assert B.fusedops_rendezvous_error(ws) == (B.OK, 1)          # sticky until cleared
+    assert B.fusedops_rendezvous_error(ws, clear=True) == (B.OK, 1)
+    assert B.fusedops_rendezvous_error(ws) == (B.OK, 0)
+
+
 @pytest.mark.parametrize("M,N,K", [(40, 4160, 64), (300, 1056, 136), (2300, 8192, 128)])
 def test_fp8_workspace_reused_across_calls(M, N, K):
     """One workspace, several quantised calls in a row on different inputs (the release
