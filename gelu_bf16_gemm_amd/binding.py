@@ -44,7 +44,9 @@ LN_MAX_COLS = 16384
 # every symbol the public header declares
 EXPORTS = ("fusedops_linear_epilogue", "fusedops_linear_workspace_bytes", "fusedops_layernorm_gelu",
            "fusedops_rmsnorm_finalize", "fusedops_cross_entropy_finalize", "fusedops_partial_cols",
-           "fusedops_abi_version", "fusedops_status_string", "fusedops_rendezvous_error")
+           "fusedops_abi_version", "fusedops_status_string", "fusedops_rendezvous_error",
+           "fusedops_linear_epilogue_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class Op(ctypes.Structure):
@@ -61,6 +63,9 @@ _i64, _i32, _vp, _f32, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ct
 lib.fusedops_linear_epilogue.restype = _i32
 lib.fusedops_linear_epilogue.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32,
                                          ctypes.POINTER(Op), _i32, _vp, _i64, _i32, _vp, _sz, _vp]
+lib.fusedops_linear_epilogue_noalloc.restype = _i32
+lib.fusedops_linear_epilogue_noalloc.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32,
+                                                 ctypes.POINTER(Op), _i32, _vp, _i64, _i32, _vp]
 lib.fusedops_linear_workspace_bytes.restype = _sz
 lib.fusedops_linear_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.POINTER(Op), _i32]
 lib.fusedops_layernorm_gelu.restype = _i32
@@ -184,6 +189,21 @@ def fusedops_linear_epilogue(x, w, y, *, bias=None, ops=(), workspace=None, out_
     return lib.fusedops_linear_epilogue(
         x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), _ptr(bias), M, N, K, dtype_code(x), arr, n,
         _ptr(y), _ld(y) if y is not None else 0, od, _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def fusedops_linear_epilogue_noalloc(x, w, y, *, bias=None, ops=(), out_dtype=None, stream=None) -> int:
+    """fusedops_linear_epilogue without a workspace: FP8 rendezvous state in the library's
+    per-GPU device array (for callers that cannot allocate)."""
+    M, K = x.shape
+    N = w.shape[0]
+    arr, n = op_array(list(ops))
+    od = out_dtype if out_dtype is not None else (dtype_code(y) if y is not None else None)
+    if od is None:
+        split = [o for o in ops if o.kind == OP_SPLIT_COLS]
+        od = split[0].dtype if split else F32
+    return lib.fusedops_linear_epilogue_noalloc(
+        x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), _ptr(bias), M, N, K, dtype_code(x), arr, n,
+        _ptr(y), _ld(y) if y is not None else 0, od, _stream(stream))
 
 
 def prepare_linear_epilogue(x, w, y, *, bias=None, ops=(), workspace=None, out_dtype=None, stream=None):

@@ -24,6 +24,7 @@ SOURCES = [
     "layernorm_gelu.hip",
     "rmsnorm_finalize.hip",
     "xent_finalize.hip",
+    "noalloc.hip",
     "api.cpp",
 ]
 

@@ -133,11 +133,13 @@ size_t fusedops_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, const fu
   return ol.quant ? ws_bytes_for(M, N) : 0;
 }
 
-int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int64_t ldw,
-                                 const void* bias, int64_t M, int64_t N, int64_t K,
-                                 int32_t in_dtype, const fusedops_op* ops, int32_t n_ops, void* Y,
-                                 int64_t ldy, int32_t out_dtype, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+// The fused linear call. With clear_ws (the allocation-free entry point, whose workspace is the
+// library's shared device scratch) a quantised call first zeroes the scratch's counters on the
+// stream, since the previous call may have used another N's layout.
+static int32_t linear_call(const void* X, int64_t ldx, const void* W, int64_t ldw, const void* bias, int64_t M,
+                           int64_t N, int64_t K, int32_t in_dtype, const fusedops_op* ops, int32_t n_ops, void* Y,
+                           int64_t ldy, int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                           bool clear_ws) {
   // ---- scalars and enums
   if (!X || !W) return FUSEDOPS_ERR_INVALID_ARG;
   if (M < 1 || N < 1 || K < 1) return FUSEDOPS_ERR_INVALID_ARG;
@@ -387,6 +389,12 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (clear_ws && ol.quant) {
+    if (int32_t st = launch_status(launch_clear_rendezvous(workspace, cdiv(M, 32), (int)(32 * (2 + ws_groups(N))),
+                                                           ws_block_words(N), s),
+                                   "clear_rendezvous"))
+      return st;
+  }
   switch (kern) {
     case Kernel::T256: return launch_status(launch_gemm_bf16_t256(a, s), "gemm_bf16_t256");
     case Kernel::SKINNY: return launch_status(launch_gemm_bf16_skinny(a, s), "gemm_bf16_skinny");
@@ -396,7 +404,11 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
 }
 
 int32_t fusedops_rendezvous_error(void* workspace, int32_t clear, int32_t* error, void* stream) {
-  if (!workspace || !error) return FUSEDOPS_ERR_INVALID_ARG;
+  if (!error) return FUSEDOPS_ERR_INVALID_ARG;
+  if (!workspace) {
+    // the no-allocation entry point's scratch on the current device
+    if (hipError_t e = noalloc_scratch(&workspace)) return launch_status(e, "no-allocation scratch lookup");
+  }
   if (!aligned(workspace, 16)) return FUSEDOPS_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t word = 0;
@@ -411,6 +423,32 @@ int32_t fusedops_rendezvous_error(void* workspace, int32_t clear, int32_t* error
   }
   *error = word != 0 ? 1 : 0;
   return FUSEDOPS_OK;
+}
+
+int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int64_t ldw,
+                                 const void* bias, int64_t M, int64_t N, int64_t K,
+                                 int32_t in_dtype, const fusedops_op* ops, int32_t n_ops, void* Y,
+                                 int64_t ldy, int32_t out_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return linear_call(X, ldx, W, ldw, bias, M, N, K, in_dtype, ops, n_ops, Y, ldy, out_dtype, workspace,
+                     workspace_bytes, stream, false);
+}
+
+int32_t fusedops_linear_epilogue_noalloc(const void* X, int64_t ldx, const void* W, int64_t ldw,
+                                         const void* bias, int64_t M, int64_t N, int64_t K, int32_t in_dtype,
+                                         const fusedops_op* ops, int32_t n_ops, void* Y, int64_t ldy,
+                                         int32_t out_dtype, void* stream) {
+  // The scratch is only needed (and only looked up) for quantised op lists; a size beyond it is
+  // reported as a workspace error before anything is enqueued.
+  OpList ol;
+  if (parse_ops(ops, n_ops, ol) != FUSEDOPS_OK || !ol.quant)
+    return linear_call(X, ldx, W, ldw, bias, M, N, K, in_dtype, ops, n_ops, Y, ldy, out_dtype, nullptr, 0,
+                       stream, false);
+  if (M >= 1 && N >= 1 && ws_bytes_for(M, N) > FUSEDOPS_NOALLOC_SCRATCH_BYTES) return FUSEDOPS_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (hipError_t e = noalloc_scratch(&scratch)) return launch_status(e, "no-allocation scratch lookup");
+  return linear_call(X, ldx, W, ldw, bias, M, N, K, in_dtype, ops, n_ops, Y, ldy, out_dtype, scratch,
+                     FUSEDOPS_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 int32_t fusedops_layernorm_gelu(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows,

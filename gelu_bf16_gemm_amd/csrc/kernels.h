@@ -39,6 +39,14 @@ int gemm_f32_tile_f(const GemmArgs& a);
 int gemm_f32_threads();
 const void* gemm_f32_symbol(const GemmArgs& a);
 
+// The device array behind fusedops_linear_epilogue_noalloc (FUSEDOPS_NOALLOC_SCRATCH_BYTES on
+// each GPU): its address on the current device, looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+// Zero the ticket counter and the control lines of `records` rendezvous records (ctl_words
+// words at the start of each record_words-word record) of a workspace, on `stream`.
+hipError_t launch_clear_rendezvous(void* ws, int64_t records, int ctl_words, int64_t record_words,
+                                   hipStream_t stream);
+
 struct LnArgs {
   const void* x; int64_t ldx;
   void* y; int64_t ldy;

@@ -36,11 +36,14 @@
 extern "C" {
 #endif
 
-#define FUSEDOPS_ABI_VERSION 4
+#define FUSEDOPS_ABI_VERSION 5
 /* Width of one RMSNorm row partial: p[m,t] covers columns [128 t, 128 t + 128). */
 #define FUSEDOPS_PARTIAL_COLS 128
 /* Column width of the cross-entropy chunk statistics (XENT). */
 #define FUSEDOPS_XENT_COLS 64
+/* Bytes of the per-GPU device array fusedops_linear_epilogue_noalloc keeps its FP8 rendezvous
+ * state in (32 MiB: quantised calls up to about M N = 2^29, e.g. 16384 x 16384 on 16384 tokens). */
+#define FUSEDOPS_NOALLOC_SCRATCH_BYTES (32u << 20)
 /* Largest LayerNorm row supported by fusedops_layernorm_gelu (elements). */
 #define FUSEDOPS_LN_MAX_COLS 16384
 
@@ -205,6 +208,30 @@ int32_t fusedops_linear_epilogue(const void* X, int64_t ldx, const void* W, int6
                                  void* Y, int64_t ldy, int32_t out_dtype,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fusedops_linear_epilogue_noalloc — fusedops_linear_epilogue for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, rules and results, without the workspace pair.
+ *
+ *   QUANT_FP8_ROW's rendezvous state (what the workspace holds in fusedops_linear_epilogue) lives
+ *   in a library-owned device array of FUSEDOPS_NOALLOC_SCRATCH_BYTES that each GPU the library
+ *   runs on holds from the first such call until the process ends. A quantised call first
+ *   enqueues a small kernel that zeroes the array's counters, then the GEMM: two launches, no
+ *   hipMalloc, hipFree or other allocating call. Op lists without QUANT_FP8_ROW use no array
+ *   and launch exactly what fusedops_linear_epilogue launches.
+ *   Every call on one GPU shares its array, so calls that may overlap in time on one GPU (on
+ *   different streams) race and must not be issued; calls on one stream are ordered.
+ *   A quantised call needing more than the array (fusedops_linear_workspace_bytes of the same
+ *   call above FUSEDOPS_NOALLOC_SCRATCH_BYTES) returns FUSEDOPS_ERR_WORKSPACE, enqueuing
+ *   nothing. The array's error word is sticky across calls: read it with
+ *   fusedops_rendezvous_error(NULL, ...).
+ * Errors: as fusedops_linear_epilogue; LAUNCH also when the array's address lookup fails.
+ */
+int32_t fusedops_linear_epilogue_noalloc(const void* X, int64_t ldx, const void* W, int64_t ldw,
+                                         const void* bias, int64_t M, int64_t N, int64_t K,
+                                         int32_t in_dtype, const fusedops_op* ops, int32_t n_ops,
+                                         void* Y, int64_t ldy, int32_t out_dtype, void* stream);
+
 /* Bytes of workspace the same call needs (0 if none). Returns 0 for an invalid op list too;
  * the call itself then reports the error. */
 size_t fusedops_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, const fusedops_op* ops,
@@ -219,13 +246,14 @@ size_t fusedops_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, const fu
  * still finishes but sets the workspace's error word. Kernel faults cannot be returned by the
  * asynchronous call itself, so this query reports them.
  *
- *   workspace  a workspace passed to fusedops_linear_epilogue (device pointer, 16-byte aligned).
+ *   workspace  a workspace passed to fusedops_linear_epilogue (device pointer, 16-byte aligned),
+ *              or NULL for the device array of fusedops_linear_epilogue_noalloc on the current GPU.
  *   clear      non-zero: reset the error word to 0 after reading it.
  *   error      host output: 0 if every rendezvous since the word was last cleared completed,
  *              1 if one gave up (the quantised output of that call is unreliable).
  *   stream     synchronised before the word is read (the query waits for the calls on it).
- * Allocates nothing. Errors: INVALID_ARG (null workspace or error), MISALIGNED, LAUNCH (a HIP
- * copy or synchronisation failed; *error is then untouched).
+ * Allocates nothing. Errors: INVALID_ARG (null error), MISALIGNED, LAUNCH (a HIP copy,
+ * synchronisation or the array's lookup failed; *error is then untouched).
  */
 int32_t fusedops_rendezvous_error(void* workspace, int32_t clear, int32_t* error, void* stream);
 

@@ -32,14 +32,15 @@ def test_header_symbols_are_exported():
 
 
 def test_constants():
-    assert B.abi_version() == 4
+    assert B.abi_version() == 5
     assert B.partial_cols() == 128
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(B.status_string(s), str) and B.status_string(s)
     assert B.status_string(0) == "ok"
     text = open(HEADER).read()
     assert "#define FUSEDOPS_PARTIAL_COLS 128" in text
-    assert "#define FUSEDOPS_ABI_VERSION 4" in text
+    assert "#define FUSEDOPS_ABI_VERSION 5" in text
+    assert "#define FUSEDOPS_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
 
 
 def lin(X=addr(0), ldx=64, W=addr(1), ldw=64, bias=None, M=32, N=64, K=64, in_dt=B.BF16, ops=(),
@@ -254,10 +255,29 @@ def test_quant_workspace_limit():
 
 def test_rendezvous_error_rules():
     err = ctypes.c_int32(7)
-    assert B.lib.fusedops_rendezvous_error(None, 0, ctypes.byref(err), None) == B.ERR_INVALID_ARG
     assert B.lib.fusedops_rendezvous_error(addr(7), 0, None, None) == B.ERR_INVALID_ARG
+    assert B.lib.fusedops_rendezvous_error(None, 0, None, None) == B.ERR_INVALID_ARG
     assert B.lib.fusedops_rendezvous_error(addr(7, 4), 0, ctypes.byref(err), None) == B.ERR_MISALIGNED
     assert err.value == 7   # untouched on an argument error
+
+
+def test_noalloc_size_limit_and_plain_rules():
+    """The allocation-free entry point refuses a quantised call whose rendezvous state would not
+    fit its device array, before any HIP call; its other argument checks are the regular ones."""
+    q = mkop(B.OP_QUANT_FP8_ROW, dtype=B.F32, out=addr(6))
+    sw = mkop(B.OP_SWIGLU)
+    M, N, K = 1 << 15, 1 << 15, 64
+    assert B.fusedops_linear_workspace_bytes(M, N, K, [sw, q]) > B.NOALLOC_SCRATCH_BYTES
+    arr, n = B.op_array([sw, q])
+    st = B.lib.fusedops_linear_epilogue_noalloc(addr(0), K, addr(1), K, None, M, N, K, B.BF16, arr, n, addr(2),
+                                                N // 2, B.F8E4M3, None)
+    assert st == B.ERR_WORKSPACE
+    # no quantisation: the regular checks, nothing looked up (invalid leading dimension, null X)
+    arr, n = B.op_array([mkop(B.OP_GELU_ERF)])
+    assert B.lib.fusedops_linear_epilogue_noalloc(addr(0), 32, addr(1), 64, None, 32, 64, 64, B.BF16, arr, n,
+                                                  addr(2), 64, B.BF16, None) == B.ERR_INVALID_ARG
+    assert B.lib.fusedops_linear_epilogue_noalloc(None, 64, addr(1), 64, None, 32, 64, 64, B.BF16, arr, n,
+                                                  addr(2), 64, B.BF16, None) == B.ERR_INVALID_ARG
 
 
 def test_aliasing_rules():

@@ -1,0 +1,89 @@
+"""The allocation-free entry point against the regular one, through the C ABI.
+
+fusedops_linear_epilogue_noalloc runs the same kernels as fusedops_linear_epilogue with the FP8
+rendezvous state in the library's per-GPU device array instead of a caller workspace, so its
+outputs must equal the regular call's bit for bit (the parity bar of the regular call, which
+the rest of the suite checks against the oracle, carries over). Two quantised calls run in a
+row on one stream, the second with a smaller input and another N (another record layout in the
+shared array), on the few-token kernel and on the 256-wide tile kernel.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gelu_bf16_gemm_amd import inputs as I
+
+from helpers import Guarded, dev, host64, note
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gelu_bf16_gemm_amd import binding as B  # noqa: E402
+
+
+def inputs(M, N, K, seed):
+    rng = np.random.default_rng([707, M, N, K, seed])
+    X = dev(I.random_stored(rng, (M, K), I.BF16), I.BF16)
+    W = dev(I.random_stored(rng, (N, K), I.BF16, std=1 / math.sqrt(K)), I.BF16)
+    b = dev(I.random_stored(rng, (N,), I.BF16, std=0.5), I.BF16)
+    return X, W, b
+
+
+def quant_pair(M, N, K, seed):
+    """(codes, scales) from the regular call with its own workspace and from the allocation-free
+    call, for SwiGLU + FP8 rows."""
+    X, W, _ = inputs(M, N, K, seed)
+    res = []
+    for noalloc in (False, True):
+        y = Guarded(M, N // 2, I.F8E4M3)
+        s = Guarded(1, M, I.F32)
+        ops = [B.op(B.OP_SWIGLU), B.op(B.OP_QUANT_FP8_ROW, out=s.view[0])]
+        note(f"no-alloc pair M={M} N={N} K={K} noalloc={noalloc}")
+        if noalloc:
+            st = B.fusedops_linear_epilogue_noalloc(X, W, y.view, ops=ops, out_dtype=I.F8E4M3)
+        else:
+            ws = torch.zeros(B.fusedops_linear_workspace_bytes(M, N, K, ops) // 4, dtype=torch.int32, device="cuda")
+            st = B.fusedops_linear_epilogue(X, W, y.view, ops=ops, workspace=ws, out_dtype=I.F8E4M3)
+        assert st == B.OK, B.status_string(st)
+        torch.cuda.synchronize()
+        assert y.intact() and s.intact()
+        res.append((host64(y.view), host64(s.view[0])))
+    return res
+
+
+@pytest.mark.parametrize("first,second", [((64, 4096, 512), (17, 1024, 256)),     # few-token kernel
+                                          ((600, 2048, 256), (300, 1056, 136))])  # 256 x 256 tiles
+def test_noalloc_matches_regular_entry_point(first, second):
+    for shape in (first, second):
+        (qa, sa), (qb, sb) = quant_pair(*shape, seed=1)
+        assert np.array_equal(sa, sb), f"{shape}: scales differ"
+        assert np.array_equal(qa, qb), f"{shape}: codes differ"
+        assert (sa > 0).all()
+    assert B.fusedops_rendezvous_error(None) == (B.OK, 0)
+
+
+def test_noalloc_without_quantisation_is_the_regular_call():
+    M, N, K = 300, 264, 136
+    X, W, b = inputs(M, N, K, 2)
+    ya, yb = Guarded(M, N, I.BF16), Guarded(M, N, I.BF16)
+    note("no-alloc bias + gelu")
+    assert B.fusedops_linear_epilogue(X, W, ya.view, bias=b, ops=[B.op(B.OP_GELU_ERF)]) == B.OK
+    assert B.fusedops_linear_epilogue_noalloc(X, W, yb.view, bias=b, ops=[B.op(B.OP_GELU_ERF)]) == B.OK
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view, yb.view) and ya.intact() and yb.intact()
+
+
+def test_noalloc_refuses_calls_beyond_its_array():
+    M, N, K = 1 << 15, 1 << 15, 64
+    X = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    W = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, N // 2), dtype=torch.uint8, device="cuda")
+    s = torch.empty(M, dtype=torch.float32, device="cuda")
+    ops = [B.op(B.OP_SWIGLU), B.op(B.OP_QUANT_FP8_ROW, out=s)]
+    assert B.fusedops_linear_workspace_bytes(M, N, K, ops) > B.NOALLOC_SCRATCH_BYTES
+    assert B.fusedops_linear_epilogue_noalloc(X, W, y, ops=ops, out_dtype=I.F8E4M3) == B.ERR_WORKSPACE
