@@ -7,11 +7,17 @@ residual + RMSNorm partials + finalize, the gate/up SwiGLU, and the decode / pre
 SwiGLU + FP8 row quantisation, plus the small fp32 Linear+GELU).
 
 `value` is the fused GEMM+epilogue throughput of the step in TFLOP/s: the sum of 2MNK
-over the GEMM workloads divided by their summed average launch time. Each workload's
-own TFLOP/s or GB/s and roofline fraction is reported beside it. Launch times are
-taken with HIP events on the stream the kernels run on, averaged over the timed
-launches; inputs rotate over several copies so operands do not stay resident in the
-256 MB last-level cache between launches.
+over the GEMM workloads divided by their summed launch time. Each workload's own TFLOP/s
+or GB/s and roofline fraction is reported beside it. A workload's launch time is the median
+of 5 repetitions, each the average of `--steps` launches bracketed by HIP events on the
+stream the kernels run on; inputs rotate over several copies so operands do not stay
+resident in the 256 MB last-level cache between launches.
+
+After each workload's timing, its oracle leg runs the fp64 oracle on sampled rows: the
+time it takes is that workload's `cpu_baseline`, and the GPU's outputs for the same rows
+are compared with it by the test suite's rules. A workload whose outputs fail reports no
+rate and leaves `value`. (`--no-cpu-baseline` skips the oracle legs: "parity": "not
+checked".)
 
 Prints one JSON line.
 """
@@ -23,6 +29,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -62,15 +69,17 @@ NEXT = [
 
 
 SETTLE_MS = 100.0
+REPS = 5
 
 
-def time_workload(run, steps: int, warmup: int, settle_ms: float = SETTLE_MS) -> float:
-    """Average launch time in ms over `steps` launches after an untimed warm-up of at least
-    `warmup` launches and at least `settle_ms` of launches. The GPU idles while a workload's
-    inputs are made on the host, and after an idle spell its clock takes a few tens of ms of
-    load to settle (measured: the first 50 ms of MLP-up launches run up to 25 % slower, the
-    first 20 ms of QKV launches up to 3x on the first one); the timed launches are the steady
-    state a loop of such layers runs in."""
+def time_workload(run, steps: int, warmup: int, settle_ms: float = SETTLE_MS, reps: int = REPS) -> list:
+    """Average launch time in ms of each of `reps` repetitions of `steps` launches, after an
+    untimed warm-up of at least `warmup` launches and at least `settle_ms` of launches. The GPU
+    idles while a workload's inputs are made on the host, and after an idle spell its clock takes
+    a few tens of ms of load to settle (measured: the first 50 ms of MLP-up launches run up to
+    25 % slower, the first 20 ms of QKV launches up to 3x on the first one); the timed launches
+    are the steady state a loop of such layers runs in. Each repetition is bracketed by HIP
+    events on the stream the kernels run on (torch's current stream, which the binding passes)."""
     import torch
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -80,15 +89,19 @@ def time_workload(run, steps: int, warmup: int, settle_ms: float = SETTLE_MS) ->
         i += 1
         if i % 4 == 0:
             torch.cuda.synchronize()    # the wall clock follows the GPU, not the enqueueing
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()                      # torch's current stream: the stream the binding launches on
-    for j in range(steps):
-        run.launch(i + j)
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    out = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for j in range(steps):
+            run.launch(i + j)
+        end.record()
+        torch.cuda.synchronize()
+        i += steps
+        out.append(start.elapsed_time(end) / steps)
+    return out
 
 
 def copies_for(spec) -> int:
@@ -104,12 +117,25 @@ def copies_for(spec) -> int:
     return max(1, min(8, -(-(300 << 20) // max(per, 1))))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] + [1]))
+
+
 def cpu_baseline(seconds_target: float = 10.0, seconds_cap: float = 30.0) -> dict:
     """The oracle (unchanged) on the dominant workload: whole passes over its M rows in
     1024-row blocks until at least `seconds_target` of oracle time (stopping early once
     `seconds_cap` is passed). Input generation is outside the timed region."""
-    from threadpoolctl import threadpool_info
-
     import oracle as O
     from gelu_bf16_gemm_amd import inputs as I
 
@@ -132,11 +158,70 @@ def cpu_baseline(seconds_target: float = 10.0, seconds_cap: float = 30.0) -> dic
         passes += 1
         if t_total > seconds_cap:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     flops = 2.0 * total_rows * N * K
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "oracle": "numpy float64 with a BLAS matmul for the contraction, scipy's erfc (the oracle as written)",
             "sample": f"{total_rows} rows ({passes} pass(es) over the {M} rows of {DOMINANT} in "
                       f"{block}-row blocks; bias + GELU erf, fp64), {t_total:.1f} s of oracle time"}
+
+
+def sample_rows(M: int, n: int = 48) -> "np.ndarray":
+    """The first and last 8 rows and a seeded spread between them."""
+    import numpy as np
+    rng = np.random.default_rng([505, M])
+    return np.array(sorted(set(range(min(8, M))) | set(range(max(0, M - 8), M)) |
+                           set(rng.integers(0, M, n).tolist())))
+
+
+def oracle_leg(name: str, spec: dict, inp: dict, run) -> dict:
+    """The oracle on sampled rows of the workload just timed: its time on those rows (this
+    workload's cpu_baseline) and the parity gate of the GPU's outputs for the same rows (every
+    output of each sampled row, by the comparison rules of the test suite)."""
+    import oracle as O  # noqa: F401  (the oracle leg: the only part of this script that runs it)
+    from oracle import parity as P
+
+    from gelu_bf16_gemm_amd import inputs as I
+
+    rows = sample_rows(spec["M"] if "M" in spec else spec["rows"])
+    t0 = time.perf_counter()
+    if spec["kind"] == "ln":
+        dt = spec["io_dtype"]
+        ref = O.layernorm_gelu(I.to_f64(inp["x"][rows], dt), I.to_f64(inp["gamma"], dt), I.to_f64(inp["beta"], dt),
+                               spec["eps"], spec["form"])
+        t = time.perf_counter() - t0
+        work, unit = 4.0 * len(rows) * spec["cols"], "GB/s"
+        check = lambda: P.check_out(run.outputs(rows), ref, spec["io_dtype"], name)  # noqa: E731
+    elif spec["kind"] == "chain":
+        out = run.outputs(rows)
+        t0 = time.perf_counter()
+        try:
+            P.check_chain_rows(spec, inp, rows, out, name=name)   # the oracle and the comparison together
+            failed = None
+        except AssertionError as e:
+            failed = e
+        t = time.perf_counter() - t0
+        work, unit = 2.0 * len(rows) * (spec["d"] * spec["K0"] + spec["N2"] * spec["d"]), "TFLOP/s"
+
+        def check():
+            if failed is not None:
+                raise failed
+    else:
+        W64 = P.decode_weights(spec, inp)
+        t0 = time.perf_counter()
+        P.linear_rows(spec, inp, rows, W64)
+        t = time.perf_counter() - t0
+        work, unit = 2.0 * len(rows) * spec["N"] * spec["K"], "TFLOP/s"
+        check = lambda: P.check_linear_rows(spec, inp, rows, run.outputs(rows), W64=W64, name=name)  # noqa: E731
+    parity = "pass"
+    try:
+        check()
+    except AssertionError as e:
+        parity = f"FAIL: {str(e)[:300]}"
+    rate = work / t / (1e12 if unit == "TFLOP/s" else 1e9)
+    return {"parity": parity, "parity_rows": int(len(rows)),
+            "cpu_baseline": {"value": round(rate, 4), "unit": unit, "seconds": round(t, 4), "rows": int(len(rows)),
+                             "kind": "oracle"}}
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -210,15 +295,19 @@ def main() -> int:
         spec = I.WORKLOADS[name]
         print(f"[bench] {name}: inputs", file=sys.stderr, flush=True)
         if spec["kind"] == "ln":
-            run = WL.LnRun(spec, I.make_ln_inputs(spec), copies=copies_for(spec))
+            inp = I.make_ln_inputs(spec)
+            run = WL.LnRun(spec, inp, copies=copies_for(spec))
         elif spec["kind"] == "chain":
-            run = WL.ChainRun(spec, I.make_chain_inputs(spec), copies=copies_for(spec))
+            inp = I.make_chain_inputs(spec)
+            run = WL.ChainRun(spec, inp, copies=copies_for(spec))
         else:
-            run = WL.LinearRun(spec, I.make_linear_inputs(spec), copies=copies_for(spec))
+            inp = I.make_linear_inputs(spec)
+            run = WL.LinearRun(spec, inp, copies=copies_for(spec))
         print(f"[bench] {name}: timing", file=sys.stderr, flush=True)
-        ms = time_workload(run, args.steps, args.warmup)
+        reps = time_workload(run, args.steps, args.warmup)
+        ms = statistics.median(reps)
         fl, by = run.flops(), run.bytes()
-        r = {"ms": round(ms, 5), "bound": bound.get(name, "mfma")}
+        r = {"ms": round(ms, 5), "ms_reps": [round(x, 5) for x in reps], "bound": bound.get(name, "mfma")}
         if fl:
             r["TFLOP/s"] = round(fl / ms / 1e9, 2)
             peak = {I.F32: PEAK_F32_TFLOPS, I.F8E4M3: PEAK_FP8_TFLOPS}.get(spec.get("in_dtype"), PEAK_BF16_TFLOPS)
@@ -226,12 +315,22 @@ def main() -> int:
         r["bytes"] = int(by)
         r["GB/s"] = round(by / ms / 1e6, 1)
         r["hbm_frac"] = round(by / ms / 1e6 / PEAK_HBM_GBPS, 4)
+        if args.no_cpu_baseline:
+            r["parity"] = "not checked"
+        else:
+            print(f"[bench] {name}: oracle on sampled rows (cpu baseline + parity gate)", file=sys.stderr, flush=True)
+            r.update(oracle_leg(name, spec, inp, run))
+            if r["parity"] != "pass":
+                # a rate is reported only for outputs that match the oracle
+                for k in ("TFLOP/s", "mfma_frac", "GB/s", "hbm_frac"):
+                    r[k] = None
         results[name] = r
-        del run
+        del run, inp
         torch.cuda.empty_cache()
         print(f"[bench] {name}: {r}", file=sys.stderr, flush=True)
 
-    gemm = [n for n in names if I.WORKLOADS[n]["kind"] == "linear" and n in suite]
+    gemm = [n for n in names if I.WORKLOADS[n]["kind"] == "linear" and n in suite
+            and results[n].get("parity") in ("pass", "not checked")]
     gemm_ms = sum(results[n]["ms"] for n in gemm)
     gemm_flops = sum(2.0 * I.WORKLOADS[n]["M"] * I.WORKLOADS[n]["N"] * I.WORKLOADS[n]["K"] for n in gemm)
     value = gemm_flops / gemm_ms / 1e9 if gemm_ms > 0 else 0.0
@@ -248,7 +347,8 @@ def main() -> int:
     ln = results.get("ln_gelu_f16_32768x4096")
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "warmup_min_ms": SETTLE_MS,
+        "warmup": args.warmup, "warmup_min_ms": SETTLE_MS, "repetitions": REPS,
+        "timing": f"per workload: median of {REPS} repetitions of `steps` launches, each bracketed by HIP events",
         "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "fused-linear hot path suite (one pass of every workload at full size)",

@@ -57,3 +57,42 @@ def test_committed_profiles_parse():
         assert rec["traffic_bytes_per_launch"] > 0
         n += 1
     assert n >= 1
+
+
+class _FakeRun:
+    """Stands in for a workload runner: returns given outputs for the sampled rows."""
+
+    def __init__(self, fn):
+        self.fn = fn
+
+    def outputs(self, rows):
+        return self.fn(rows)
+
+
+def test_oracle_leg_gates_on_parity():
+    """The oracle leg passes outputs equal to the oracle's and fails (so the rate is withheld)
+    for outputs 1 % off; it reports the oracle's own rate on the sampled rows."""
+    import numpy as np
+
+    from gelu_bf16_gemm_amd import inputs as I
+    from oracle import parity as P
+
+    name = "linear_gelu_f32_64x256x256"
+    spec = I.WORKLOADS[name]
+    inp = I.make_linear_inputs(spec)
+    good = _FakeRun(lambda rows: {"y": P.linear_rows(spec, inp, rows)["y"]})
+    bad = _FakeRun(lambda rows: {"y": P.linear_rows(spec, inp, rows)["y"] * 1.01})
+    r = bench.oracle_leg(name, spec, inp, good)
+    assert r["parity"] == "pass" and r["parity_rows"] == len(bench.sample_rows(64))
+    assert r["cpu_baseline"]["kind"] == "oracle" and r["cpu_baseline"]["value"] > 0
+    assert bench.oracle_leg(name, spec, inp, bad)["parity"].startswith("FAIL")
+    ln = "ln_gelu_f16_32768x3000"
+    lspec = dict(I.WORKLOADS[ln], rows=64)
+    linp = I.make_ln_inputs(lspec)
+    import oracle as O
+    ref = lambda rows: O.layernorm_gelu(I.to_f64(linp["x"][rows], I.F16), I.to_f64(linp["gamma"], I.F16),  # noqa: E731
+                                        I.to_f64(linp["beta"], I.F16), 1e-5, "tanh")
+    assert bench.oracle_leg(ln, lspec, linp, _FakeRun(ref))["parity"] == "pass"
+    assert bench.oracle_leg(ln, lspec, linp, _FakeRun(lambda rows: ref(rows) + 0.1))["parity"].startswith("FAIL")
+    rows = bench.sample_rows(16384)
+    assert rows[0] == 0 and rows[-1] == 16383 and len(rows) > 50 and np.all(np.diff(rows) > 0)
