@@ -315,16 +315,19 @@ __device__ __forceinline__ void load8(const void* base, int dtype, int64_t idx, 
   }
 }
 
+// Outputs are written once and not read again by this kernel: nontemporal stores, so they do
+// not stay in L2 as dirty lines that later operand loads would have to evict.
 __device__ __forceinline__ void store8(void* base, int dtype, int64_t idx, const float (&v)[8]) {
   if (dtype == FUSEDOPS_F32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx));
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]},
+                                reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx + 4));
   } else {
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       o[j] = dtype == FUSEDOPS_BF16 ? pack_bf16x2(v[2 * j], v[2 * j + 1]) : pack_f16x2(v[2 * j], v[2 * j + 1]);
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + idx) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + idx));
   }
 }
 
@@ -418,7 +421,7 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     // activation; SwiGLU leaves its 4 outputs in v[0..3]
     if (e.act == ACT_GELU_ERF) {
       // fp32 outputs keep fp32 relative accuracy in the negative tail; 16-bit and E4M3
-      // outputs take the shorter A&S form, whose error is far below their rounding
+      // outputs take the one-exp2 form, whose error is far below their rounding
       if (e.y_dtype == FUSEDOPS_F32) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = gelu_erf_precise_f32(v[i]);
