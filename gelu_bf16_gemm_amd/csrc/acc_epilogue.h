@@ -226,12 +226,22 @@ __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int r
     if (whole) {
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(d.at(seg) + ((int64_t)t * d.ld + cseg) * d.es));
     } else {
+      // the row's last chunk (or one crossing a split boundary): whole 4-byte words, then
+      // single elements of a word the output ends in (rows need not end on a word)
+      const int nel = 4 / d.es;  // elements per word
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const int cw = col + w * 4 / d.es;  // first column of word w
+        const int cw = col + w * nel;  // first column of word w
         if (cw >= d.cols) break;
         const int sg = sw ? cw / sw : 0;
-        *reinterpret_cast<uint32_t*>(d.at(sg) + ((int64_t)t * d.ld + (cw - sg * sw)) * d.es) = v[w];
+        uint8_t* p = d.at(sg) + ((int64_t)t * d.ld + (cw - sg * sw)) * d.es;
+        if (cw + nel <= d.cols) {
+          *reinterpret_cast<uint32_t*>(p) = v[w];
+        } else if (d.es == 2) {
+          *reinterpret_cast<uint16_t*>(p) = (uint16_t)v[w];   // one 2-byte element left
+        } else {
+          for (int i = 0; i < d.cols - cw; ++i) p[i] = (uint8_t)(v[w] >> (8 * i));  // 1-3 codes left
+        }
       }
     }
   }
@@ -455,9 +465,13 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
       const int rows = min(R, M - t0 - p * R);  // valid rows of this pass (>= 1 for p = 0)
       lds_barrier();
       if (rows > 0) {
+        // The range ends at the 16-byte chunk boundary after the last valid column: a load that
+        // crosses the end of the range reads as zero as a whole, which would drop the valid
+        // columns of a chunk that N cuts through. The chunk lies inside its row's storage (the
+        // leading dimension keeps rows 16-byte aligned); its columns past N are zeroed below.
         const uint8_t* zb = static_cast<const uint8_t*>(e.z) + ((int64_t)(t0 + p * R) * e.ldz + f0) * es;
-        const __amdgpu_buffer_rsrc_t rz =
-            make_rsrc(zb, (uint32_t)(((int64_t)(rows - 1) * e.ldz + min(kTileCols, N - f0)) * es));
+        const int zcols = (min(kTileCols, N - f0) + 16 / es - 1) / (16 / es) * (16 / es);
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc(zb, (uint32_t)(((int64_t)(rows - 1) * e.ldz + zcols) * es));
 #pragma unroll 8
         for (int j = 0; j < R * C / kEpiThreads; ++j) {
           const int id = j * kEpiThreads + wave * 64 + lane_u;
@@ -475,6 +489,10 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
       lds_barrier();
       if (passes == 1 || wt == p) {
+        // a 16-byte chunk that N cuts through was loaded whole: in the wave whose features reach
+        // past N (uniform), its columns past N are zeroed so they add nothing to h1 and to the
+        // row partials
+        const bool tail = f0 + wf * 128 + 128 > N;
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
@@ -482,7 +500,11 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
             f32x16 v = acc[fb][tb];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const f32x4 z = lds_get4(lds, st_off(tk(tb) - p * R, fl(fb, q) * es, C), zdt);
+              f32x4 z = lds_get4(lds, st_off(tk(tb) - p * R, fl(fb, q) * es, C), zdt);
+              if (tail) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) z[j] = f0 + fl(fb, q) + j < N ? z[j] : 0.f;
+              }
 #pragma unroll
               for (int j = 0; j < 4; ++j) v[4 * q + j] += z[j];
             }

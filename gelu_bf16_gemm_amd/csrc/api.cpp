@@ -220,7 +220,7 @@ static int32_t linear_call(const void* X, int64_t ldx, const void* W, int64_t ld
 
   // ---- alignment: 16-byte bases and rows; K and N granularity
   const int k_gran = 16 / es_in;
-  if (K % k_gran || N % 8) return FUSEDOPS_ERR_MISALIGNED;
+  if (K % k_gran) return FUSEDOPS_ERR_MISALIGNED;
   if (!aligned(X, 16) || !aligned(W, 16) || (ldx * es_in) % 16 || (ldw * es_in) % 16) return FUSEDOPS_ERR_MISALIGNED;
   if (bias && !aligned(bias, 16)) return FUSEDOPS_ERR_MISALIGNED;
   if (Y && (!aligned(Y, 16) || (ldy * es_out) % 16)) return FUSEDOPS_ERR_MISALIGNED;

@@ -331,6 +331,26 @@ __device__ __forceinline__ void store8(void* base, int dtype, int64_t idx, const
   }
 }
 
+// The last group of a row when N is not a multiple of 8: the first n (< 8) elements only; the
+// others read as 0 and are not written.
+__device__ __forceinline__ void load8_n(const void* base, int dtype, int64_t idx, int n, float (&o)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = i < n ? load1(base, dtype, idx + i) : 0.f;
+}
+
+__device__ __forceinline__ void store1(void* base, int dtype, int64_t idx, float v) {
+  if (dtype == FUSEDOPS_F32) static_cast<float*>(base)[idx] = v;
+  else if (dtype == FUSEDOPS_BF16) static_cast<uint16_t*>(base)[idx] = (uint16_t)f32_to_bf16_bits(v);
+  else static_cast<uint16_t*>(base)[idx] = (uint16_t)f32_to_f16_bits(v);
+}
+
+template <int W>
+__device__ __forceinline__ void store_n(void* base, int dtype, int64_t idx, int n, const float (&v)[W]) {
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    if (i < n) store1(base, dtype, idx + i, v[i]);
+}
+
 // ---------------------------------------------------------------------------
 // the chain over a staged tile
 // ---------------------------------------------------------------------------
@@ -358,6 +378,10 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
   const int c = g * 8;
   const int f = f0 + c;
   const bool f_ok = f < N;
+  // columns of this thread's group inside the output: 8, or fewer in the last group of a row
+  // whose width is not a multiple of 8 (the rest read as 0 and are neither stored nor reduced)
+  const int nv = f_ok ? min(8, N - f) : 0;
+  const bool full = nv == 8;
   const bool swiglu = e.act == ACT_SWIGLU;
   const bool side = mode != EPI_QUANT;
   const int zb = e.z_dtype == FUSEDOPS_F32 ? 4 : 2;
@@ -368,8 +392,14 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
   float bias[8], gam[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) { bias[i] = 0.f; gam[i] = 1.f; }
-  if (e.bias && f_ok) load8(e.bias, e.bias_dtype, f, bias);
-  if (e.gamma && f_ok) load8(e.gamma, e.gamma_dtype, f, gam);
+  if (e.bias && f_ok) {
+    if (full) load8(e.bias, e.bias_dtype, f, bias);
+    else load8_n(e.bias, e.bias_dtype, f, nv, bias);
+  }
+  if (e.gamma && f_ok) {
+    if (full) load8(e.gamma, e.gamma_dtype, f, gam);
+    else load8_n(e.gamma, e.gamma_dtype, f, nv, gam);
+  }
 
   for (int r = tid / TPR; r < nrows; r += RPI) {
     const int t = t0 + r;
@@ -395,12 +425,17 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     for (int i = 0; i < 8; ++i) v[i] += bias[i];
     if (e.z && ok) {
       float z[8];
-      load8(static_cast<const char*>(e.z) + (int64_t)t * e.ldz * zb, e.z_dtype, f, z);
+      if (full) load8(static_cast<const char*>(e.z) + (int64_t)t * e.ldz * zb, e.z_dtype, f, z);
+      else load8_n(static_cast<const char*>(e.z) + (int64_t)t * e.ldz * zb, e.z_dtype, f, nv, z);
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] += z[i];
     }
     // store-aux (h1) and its row sum-of-squares partials over 128-column chunks
-    if (side && e.aux && ok) store8(static_cast<char*>(e.aux) + (int64_t)t * e.ld_aux * ab, e.aux_dtype, f, v);
+    if (side && e.aux && ok) {
+      char* arow = static_cast<char*>(e.aux) + (int64_t)t * e.ld_aux * ab;
+      if (full) store8(arow, e.aux_dtype, f, v);
+      else store_n<8>(arow, e.aux_dtype, f, nv, v);
+    }
     if (COLS >= 128 && e.partials) {
       float s = 0.f;
 #pragma unroll
@@ -459,9 +494,9 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
       if (ok) {
         m = v[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) m = fmaxf(m, v[i]);
+        for (int i = 1; i < 8; ++i) m = i < nv ? fmaxf(m, v[i]) : m;   // columns past N left out
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sx += __builtin_amdgcn_exp2f((v[i] - m) * kLog2e);
+        for (int i = 0; i < 8; ++i) sx += i < nv ? __builtin_amdgcn_exp2f((v[i] - m) * kLog2e) : 0.f;
       }
 #pragma unroll
       for (int o = 1; o < 8; o <<= 1) {
@@ -478,7 +513,7 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
       }
       if (ok) {
         const int o = e.xent_labels[t] - f;
-        if (o >= 0 && o < 8) {
+        if (o >= 0 && o < nv) {   // labels at or past N mark ignored rows
           float val = v[0];
 #pragma unroll
           for (int i = 1; i < 8; ++i) val = o == i ? v[i] : val;
@@ -491,13 +526,21 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     if (mode == EPI_STORE) {
       if (!ok || (!e.y && !e.n_split)) continue;  // no Y: the logits are not stored (XENT)
       if (swiglu) {
-        store4(static_cast<char*>(e.y) + (int64_t)t * e.ldy * yb, e.y_dtype, fo, f32x4{v[0], v[1], v[2], v[3]});
+        char* yrow = static_cast<char*>(e.y) + (int64_t)t * e.ldy * yb;
+        if (full) {
+          store4(yrow, e.y_dtype, fo, f32x4{v[0], v[1], v[2], v[3]});
+        } else {
+          const float o4[4] = {v[0], v[1], v[2], v[3]};
+          store_n<4>(yrow, e.y_dtype, fo, nv / 2, o4);   // N is even with SwiGLU
+        }
       } else if (e.n_split) {
         const int seg = (int)(f / e.split_w);
         void* base = seg == 0 ? e.yv0 : (seg == 1 ? e.yv1 : e.yv2);
         store8(static_cast<char*>(base) + (int64_t)t * e.ldv * yb, e.y_dtype, f - (int64_t)seg * e.split_w, v);
       } else {
-        store8(static_cast<char*>(e.y) + (int64_t)t * e.ldy * yb, e.y_dtype, f, v);
+        char* yrow = static_cast<char*>(e.y) + (int64_t)t * e.ldy * yb;
+        if (full) store8(yrow, e.y_dtype, f, v);
+        else store_n<8>(yrow, e.y_dtype, f, nv, v);
       }
     } else if (mode == EPI_AMAX) {
       float m = 0.f;
@@ -518,12 +561,17 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf((v[i] * fac.pre) * fac.inv, -448.f), 448.f);
       uint8_t* yrow = static_cast<uint8_t*>(e.y) + (int64_t)t * e.ldy;
-      if (swiglu) {
-        *reinterpret_cast<uint32_t*>(yrow + fo) = pack_e4m3x2(q[0], q[1]) | (pack_e4m3x2(q[2], q[3]) << 16);
+      const u32x2 w = {pack_e4m3x2(q[0], q[1]) | (pack_e4m3x2(q[2], q[3]) << 16),
+                       pack_e4m3x2(q[4], q[5]) | (pack_e4m3x2(q[6], q[7]) << 16)};
+      if (full) {
+        if (swiglu) *reinterpret_cast<uint32_t*>(yrow + fo) = w[0];
+        else *reinterpret_cast<u32x2*>(yrow + fo) = w;
       } else {
-        const u32x2 w = {pack_e4m3x2(q[0], q[1]) | (pack_e4m3x2(q[2], q[3]) << 16),
-                         pack_e4m3x2(q[4], q[5]) | (pack_e4m3x2(q[6], q[7]) << 16)};
-        *reinterpret_cast<u32x2*>(yrow + fo) = w;
+        // the row's last group: one byte per valid code
+        const int nq = swiglu ? nv / 2 : nv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nq) yrow[fo + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
       }
     }
   }

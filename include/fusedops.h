@@ -85,6 +85,9 @@ enum fusedops_dtype {
  *
  * Fields used per kind (others ignored):
  *   RESIDUAL_ADD      in = z (M x N, dtype = op.dtype in {BF16, F16, F32}), ld = row stride of z.
+ *                     A row is read in 16-byte chunks: when N ends inside a chunk, the chunk's
+ *                     elements past N (inside the row's 16-byte-aligned storage) are read and
+ *                     ignored.
  *                     z may alias Y exactly (same pointer, same ld, same dtype) for an in-place
  *                     residual update; any other overlap with an output is not allowed.
  *   STORE_AUX         out = h1 (M x N, dtype = op.dtype in {BF16, F16, F32}), ld = row stride.
@@ -178,7 +181,10 @@ typedef struct fusedops_op {
  *          the MFMA contraction runs on E4M3 operands with fp32 accumulation).
  *   W      N x K, row stride ldw, dtype in_dtype.
  *   bias   length N, dtype in_dtype (BF16 when in_dtype is F8E4M3), or NULL for no bias.
- *   M,N,K  >= 1. K must be a multiple of 8 (BF16), 4 (F32) or 16 (F8E4M3); N a multiple of 8.
+ *   M,N,K  >= 1. K must be a multiple of 8 (BF16), 4 (F32) or 16 (F8E4M3); N is any width (an
+ *          output row may end inside a 16-byte chunk: its last elements are written singly, and
+ *          nothing past the row's N_out columns is written). Leading dimensions still keep rows
+ *          16-byte aligned.
  *   ops    n_ops ops in canonical order (n_ops = 0 allowed; ops may be NULL then).
  *   Y      M x N_out (N_out = N/2 with SWIGLU, else N), row stride ldy, dtype out_dtype
  *          in {BF16, F16, F32}, or F8E4M3 exactly when QUANT_FP8_ROW is present.

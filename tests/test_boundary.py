@@ -204,7 +204,10 @@ def test_split_rules():
 
 def test_alignment_rules():
     assert lin(K=60, ldx=64, ldw=64) == B.ERR_MISALIGNED            # K % 8 (bf16)
-    assert lin(N=60, ldy=64) == B.ERR_MISALIGNED                    # N % 8
+    assert lin(N=61, ldy=61) == B.ERR_MISALIGNED                    # Y rows not 16-byte aligned
+    # any N: N = 61 passes the alignment checks and fails only at the later workspace check
+    q = mkop(B.OP_QUANT_FP8_ROW, dtype=B.F32, out=addr(6))
+    assert lin(N=61, ldy=64, ops=[q], out_dt=B.F8E4M3) == B.ERR_WORKSPACE
     assert lin(X=addr(0, 8)) == B.ERR_MISALIGNED
     assert lin(W=addr(1, 2)) == B.ERR_MISALIGNED
     assert lin(Y=addr(2, 4)) == B.ERR_MISALIGNED

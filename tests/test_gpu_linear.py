@@ -80,7 +80,8 @@ def run_linear(M, N, K, *, in_dtype=I.BF16, out_dtype=I.BF16, bias=False, act=No
             keep["z"] = zg
             ops.append(B.op(B.OP_RESIDUAL_ADD, zg.view))
         else:
-            keep["z"] = dev(z, zdt)
+            # rows 16-byte aligned whatever N: pad the leading dimension to a multiple of 8
+            keep["z"] = upload_padded(z, zdt, (-N) % (16 // (4 if zdt == I.F32 else 2)))
             ops.append(B.op(B.OP_RESIDUAL_ADD, keep["z"]))
     if aux:
         keep["aux"] = Guarded(M, N, aux_dtype if aux_dtype is not None else zdt)
@@ -668,6 +669,37 @@ def test_gelu_erf_negative_tail_fp32_output(in_dtype, M, N, K):
     assert y.intact()
 
 
+# Any output width: rows that end inside a 16-byte chunk (N = 1001, N / 2 = 501 after SwiGLU).
+# Every output sits in a guard band, so a write past a row's last column fails the test.
+@pytest.mark.parametrize("M,N,K", [(300, 1001, 136), (40, 1001, 256), (520, 257, 264)])
+def test_odd_widths_bias_gelu(M, N, K):
+    run_linear(M, N, K, bias=True, act="gelu_erf")                                   # static / few-token
+    run_linear(M, N, K, bias=True, act="gelu_tanh", out_dtype=I.F32, seed=1)         # generic instance
+    run_linear(M, N, K, bias=True, act="gelu_erf", out_dtype=I.F16, seed=2)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 1001, 136), (40, 1001, 256)])
+def test_odd_widths_residual_partials(M, N, K):
+    run_linear(M, N, K, residual=True, aux=True, partials=True, gamma=True)
+    run_linear(M, N, K, residual=True, aux=True, partials=True, gamma=True, pad=8, seed=1)
+
+
+def test_odd_widths_fp32_kernel():
+    run_linear(70, 1001, 36, in_dtype=I.F32, out_dtype=I.F32, bias=True, residual=True, aux=True, partials=True,
+               gamma=True, act="gelu_erf")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 1002, 136), (40, 1002, 256), (600, 1026, 64)])
+def test_odd_widths_swiglu_and_fp8_rows(M, N, K):
+    run_linear(M, N, K, act="swiglu")                                                # N / 2 odd
+    run_linear(M, N, K, act="swiglu", quant=True)                                    # odd code rows
+
+
+def test_odd_widths_fp8_inputs():
+    run_linear(300, 1001, 160, in_dtype=I.F8E4M3, bias=True, act="gelu_erf")
+    run_linear(300, 1001, 160, in_dtype=I.F8E4M3, residual=True)
+
+
 # (100, 200, 600): three K chunks of 256, the last one ragged; ragged token and feature tiles
 @pytest.mark.parametrize("M,N,K", [(70, 136, 36), (1, 8, 4), (100, 200, 600)])
 def test_fp32_path_ops(M, N, K):
@@ -837,12 +869,14 @@ def run_xent(M, N, K, *, store_logits=False, bias=False, act=None, in_dtype=I.BF
         check_lowp(host64(y.view), ref, "logits")
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 1000, 136), (17, 520, 40), (129, 4096, 64), (300, 1024, 256)])
+@pytest.mark.parametrize("M,N,K", [(300, 1000, 136), (17, 520, 40), (129, 4096, 64), (300, 1024, 256),
+                                   (300, 1001, 136), (257, 50257, 256)])
 def test_xent_statistics_and_loss(M, N, K):
     run_xent(M, N, K)
 
 
 def test_xent_with_logits_bias_activation_and_fp8_inputs():
     run_xent(300, 1000, 136, store_logits=True, bias=True)
+    run_xent(300, 1001, 136, store_logits=True, bias=True, seed=3)
     run_xent(70, 512, 64, act="gelu_tanh", seed=1)
     run_xent(300, 520, 160, in_dtype=I.F8E4M3, seed=2)
