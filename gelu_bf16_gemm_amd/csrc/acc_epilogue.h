@@ -249,6 +249,17 @@ __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int r
 
 }  // namespace accepi
 
+// Keep an updated accumulator block in AGPRs. The chain visits all 16 blocks per step and keeps
+// every block between steps; left to itself the compiler holds the updated values in VGPRs,
+// runs out of them and spills to scratch, each reload then waiting with vmcnt(0) for every
+// load and store in flight. AGPRs are where the MFMAs left the blocks, and there is room.
+// (Not for the FP8 row quantisation, where the pinned blocks measured more spills and a slower
+// prefill: there the compiler's own placement is kept.)
+template <uint32_t F>
+__device__ __forceinline__ void to_agpr(f32x16& v) {
+  if constexpr ((F & epi::kStatic) != 0 && (F & epi::kQuant) == 0) asm volatile("" : "+a"(v));
+}
+
 // Run the whole epilogue of one 256 x 256 tile whose accumulators are in `acc` (the
 // layout above). `lds` is at least 128 KB of LDS that the mainloop no longer uses and
 // `svec` the tile's vectors (VecPrefetch); every thread of the workgroup must call this.
@@ -444,7 +455,10 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     for (int fb = 0; fb < 4; ++fb) {
       const f32x16 b = feat(0, fb);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[fb][tb] += b;
+      for (int tb = 0; tb < 4; ++tb) {
+        acc[fb][tb] += b;
+        to_agpr<F>(acc[fb][tb]);
+      }
     }
   }
   if (cfg.z()) {
@@ -509,6 +523,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
               for (int j = 0; j < 4; ++j) v[4 * q + j] += z[j];
             }
             acc[fb][tb] = v;
+            to_agpr<F>(acc[fb][tb]);
           }
       }
     }
@@ -539,7 +554,10 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
       f32x16 g = {};
       if (cfg.gamma()) g = feat(1, fb);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = post(acc[fb][tb], g, tb);
+      for (int tb = 0; tb < 4; ++tb) {
+        acc[fb][tb] = post(acc[fb][tb], g, tb);
+        to_agpr<F>(acc[fb][tb]);
+      }
     }
   }
 

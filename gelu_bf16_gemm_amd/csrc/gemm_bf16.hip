@@ -92,7 +92,13 @@ template <uint32_t F>
 __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, float* svec,
                                              const accepi::VecPrefetch& vp, f32x16 (&acc)[4][4], int t0, int f0) {
   constexpr int kBuf = 2 * kTileBytes;  // one stage: W tile then X tile
-  const int tid = threadIdx.x;
+  // The per-lane DMA and fragment offsets below are the same for every tile, so the compiler
+  // would compute them once, keep them live across the whole tile walk and, short of registers,
+  // spill them; each reload in the prologue then needs vmcnt(0), which also waits for every DMA
+  // and store in flight. An opaque copy of the thread index makes them per-tile values that are
+  // recomputed (a few dozen VALU ops per tile) instead.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wf = wave >> 1, wt = wave & 1;
   const int K = a.K;
