@@ -5,16 +5,17 @@
 // A workgroup owns 64 features x 32 tokens and has 8 waves. W streams in stages of
 // 64 rows x 256 K (32 KB): each load instruction reads 1 KB of memory as two 512-byte row
 // segments, so HBM is read in linear runs rather than in the row-strided 16-byte pieces
-// MFMA operands would need straight from memory. W loads run DR stages ahead in a register
-// ring, and each workgroup walks the stages in its own rotated order, so at any moment the
-// workgroups read different offsets of their rows rather than all the same one (measured:
-// deeper rings and longer stages were slower). One stage before it is needed a stage is
-// written into one of two LDS buffers, where a row's 16-byte chunk c sits at position
-// c ^ (row % 32) so that both the 64-lane writes and the 32-row MFMA operand reads are free
-// of bank conflicts. Wave w multiplies feature half w % 2 over the 64-wide K quarter w / 2
-// of every stage; its X operand (32 token rows, read by every workgroup) comes from L2
-// straight into registers, in a ring of its own. The four K-quarter partial tiles of each
-// feature half are staged in LDS and summed, in a fixed order, by the shared epilogue.
+// MFMA operands would need straight from memory. The stage's X slab (32 token rows x 256 K,
+// 16 KB, read by every workgroup and served by L2) travels the same way, once per
+// workgroup. Loads run DR stages ahead in a register ring, and each workgroup walks the
+// stages in its own rotated order, so at any moment the workgroups read different offsets
+// of their rows rather than all the same one (measured: deeper rings and longer stages were
+// slower). One stage before it is needed a stage is written into one of two LDS buffers,
+// where a row's 16-byte chunk c sits at position c ^ (row % 32) so that both the 64-lane
+// writes and the 32-row MFMA operand reads are free of bank conflicts. Wave w multiplies
+// feature half w % 2 over the 64-wide K quarter w / 2 of every stage, both operands read
+// from LDS. The four K-quarter partial tiles of each feature half are staged in LDS and
+// summed, in a fixed order, by the shared epilogue.
 #include "epilogue.h"
 #include "kernels.h"
 
@@ -28,9 +29,9 @@ constexpr int KS = 256;                      // K per stage
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowBytes = KS * 2;            // 512 bytes of a W row per stage
-constexpr int kBufBytes = BF * kRowBytes;    // 32 KB
-constexpr int DR = 2;                        // W stages in flight in registers
-constexpr int DX = 2;                        // X stages in flight in registers (L2 hits)
+constexpr int kWBytes = BF * kRowBytes;      // 32 KB of W per stage
+constexpr int kBufBytes = (BF + BT) * kRowBytes;  // 48 KB per stage buffer: W rows, then X rows
+constexpr int DR = 2;                        // stages in flight in registers
 
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_skinny_kernel(GemmArgs a) {
   // two stage buffers; afterwards they hold the 4 partial 32 x 64 fp32 tiles (32 KB) the
@@ -72,67 +73,71 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_skinny_kernel(GemmArgs 
     w_voff[i] = (uint32_t)(r * a.ldw * 2 + lc * 16);
     w_lds[i] = (uint32_t)(r * kRowBytes + ((lc ^ (r & 31)) << 4));
   }
-  // X operand of MFMA step j (0..3) of the wave's K quarter: lane half h supplies K elements
-  // [8h, 8h + 8) of the step, as the MFMA does for W
-  const uint32_t x_voff = (uint32_t)((lane & 31) * a.ldx * 2 + (kq * 64 + h * 8) * 2);
-  // W operand of step j: row wr of the stage, chunk kq * 8 + 2 j + h
-  const int wr = fb * 32 + (lane & 31);
-  uint32_t f_lds[4];
+  // X load i (0..1) of a stage: token rows 16 i + 2 wave + h, chunk lane % 32
+  uint32_t x_voff[2], x_lds[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f_lds[j] = (uint32_t)(wr * kRowBytes + (((kq * 8 + 2 * j + h) ^ (wr & 31)) << 4));
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * i + 2 * wave + h;
+    x_voff[i] = (uint32_t)(r * a.ldx * 2 + lc * 16);
+    x_lds[i] = (uint32_t)(kWBytes + r * kRowBytes + ((lc ^ (r & 31)) << 4));
+  }
+  // operands of MFMA step j (0..3) of the wave's K quarter: lane half h supplies K elements
+  // [8h, 8h + 8) of the step, i.e. chunk kq * 8 + 2 j + h of W row wr and of token row xr
+  const int wr = fb * 32 + (lane & 31), xr = lane & 31;
+  uint32_t f_lds[4], g_lds[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f_lds[j] = (uint32_t)(wr * kRowBytes + (((kq * 8 + 2 * j + h) ^ (wr & 31)) << 4));
+    g_lds[j] = (uint32_t)(kWBytes + xr * kRowBytes + (((kq * 8 + 2 * j + h) ^ xr) << 4));
+  }
 
   const int stages = (K + KS - 1) / KS;
-  u32x4 wreg[DR][4], xreg[DX][4];
-  auto load_w = [&](int s, int d) __attribute__((always_inline)) {
+  u32x4 wreg[DR][4], xreg[DR][2];
+  auto load = [&](int s, int d) __attribute__((always_inline)) {
     const uint32_t k0 = (uint32_t)(s < stages ? (s + ft) % stages : s) * KS;
     const uint32_t oob = (uint32_t)(k0 + lc * 8 >= (uint32_t)K) << 31;
 #pragma unroll
     for (int i = 0; i < 4; ++i)  // each W byte is read once: nontemporal
       wreg[d][i] = __builtin_amdgcn_raw_buffer_load_b128(rW, (w_voff[i] + k0 * 2) | oob, 0, kNonTemporal);
-  };
-  auto load_x = [&](int s, int d) __attribute__((always_inline)) {
-    const uint32_t k0 = (uint32_t)(s < stages ? (s + ft) % stages : s) * KS;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t k = k0 + kq * 64 + j * 16 + h * 8;
-      xreg[d][j] = buffer_load_16B(rX, (x_voff + (k0 + j * 16) * 2) | ((uint32_t)(k >= (uint32_t)K) << 31));
-    }
+    for (int i = 0; i < 2; ++i) xreg[d][i] = buffer_load_16B(rX, (x_voff[i] + k0 * 2) | oob);
   };
   auto put = [&](int buf, int d) __attribute__((always_inline)) {
     uint8_t* b = lds + buf * kBufBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(b + w_lds[i]) = wreg[d][i];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(b + x_lds[i]) = xreg[d][i];
   };
   f32x16 acc = {};
-  auto compute = [&](int buf, int d) __attribute__((always_inline)) {
+  auto compute = [&](int buf) __attribute__((always_inline)) {
     const uint8_t* b = lds + buf * kBufBytes;
-    bf16x8 wf[4];
+    bf16x8 wf[4], xf[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wf[j] = *reinterpret_cast<const bf16x8*>(b + f_lds[j]);
+    for (int j = 0; j < 4; ++j) {
+      wf[j] = *reinterpret_cast<const bf16x8*>(b + f_lds[j]);
+      xf[j] = *reinterpret_cast<const bf16x8*>(b + g_lds[j]);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], __builtin_bit_cast(bf16x8, xreg[d][j]), acc, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[j], acc, 0, 0, 0);
   };
 
-  // Step s handles the s-th stage of the rotated order. Stage s: its W sits in register slot
-  // s % DR and, once written, in LDS buffer s % 2; its X in slot s % DX. Step s: multiply stage s; write stage s + 1 to the other buffer (free:
-  // everyone passed the barrier after multiplying stage s - 1); load the W of stage s + DR
-  // and the X of stage s + DX into the slots stage s vacated. A stage past the last reads
-  // only zeros and adds nothing.
+  // Step s handles the s-th stage of the rotated order. Stage s sits in register slot s % DR
+  // and, once written, in LDS buffer s % 2. Step s: multiply stage s; write stage s + 1 to the
+  // other buffer (free: everyone passed the barrier after multiplying stage s - 1); load stage
+  // s + DR into slot s % DR (stage s left it when it was written to LDS a step earlier). A
+  // stage past the last reads only zeros and adds nothing.
 #pragma unroll
-  for (int d = 0; d < DR; ++d) load_w(d, d);
-#pragma unroll
-  for (int d = 0; d < DX; ++d) load_x(d, d);
+  for (int d = 0; d < DR; ++d) load(d, d);
   put(0, 0);
   __syncthreads();
   for (int s0 = 0; s0 < stages; s0 += DR) {
 #pragma unroll
     for (int d = 0; d < DR; ++d) {
       const int s = s0 + d;
-      compute(d & 1, d % DX);
+      compute(d & 1);
       put((d + 1) & 1, (d + 1) % DR);
-      load_w(s + DR, d);
-      load_x(s + DX, d % DX);
+      load(s + DR, d);
       __syncthreads();
     }
   }
