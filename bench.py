@@ -224,6 +224,21 @@ def oracle_leg(name: str, spec: dict, inp: dict, run) -> dict:
                              "kind": "oracle"}}
 
 
+def _profile_record(path: str):
+    """The machine-readable record of one committed rocprofv3 summary, and whether the sources
+    it lists are still the ones the counters were taken on (their sha256 matches)."""
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if m is None:
+        return None, False
+    rec = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for p in rec["sources"]:
+        h.update(p.encode())
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return rec, h.hexdigest() == rec["sources_sha256"]
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload` from its committed rocprofv3 summary
     (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), or None when there is no
@@ -231,16 +246,28 @@ def measured_traffic(kernel: str, workload: str):
     path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
     if not os.path.exists(path):
         return None
-    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
-    if m is None:
-        return None
-    rec = json.loads(m.group(1))
-    h = hashlib.sha256()
-    for p in rec["sources"]:
-        h.update(p.encode())
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+    rec, current = _profile_record(path)
+    return rec["traffic_bytes_per_launch"] if rec is not None and current else None
+
+
+def profile_summary(workload: str) -> dict:
+    """Per kernel of `workload`, the figures of its committed rocprofv3 summary (profiles/):
+    average duration under the trace, HBM traffic per launch, MFMA busy fraction and the clock
+    it held, resident waves per CU and LDS bank conflicts per access. Counter figures of a
+    summary whose kernel sources have changed since are withheld (null, "current": false)."""
+    out = {}
+    pdir = os.path.join(ROOT, "profiles")
+    for name in sorted(os.listdir(pdir)) if os.path.isdir(pdir) else []:
+        if not name.endswith(f"__{workload}.md"):
+            continue
+        rec, current = _profile_record(os.path.join(pdir, name))
+        if rec is None:
+            continue
+        keep = ("avg_duration_ns", "traffic_bytes_per_launch", "algorithmic_bytes_per_launch", "mfma_busy_frac",
+                "clock_ghz", "waves_per_cu", "lds_bank_conflicts_per_access")
+        out[name.split("__", 1)[0]] = {"current": current, "summary": f"profiles/{name}",
+                                       **{k: (rec.get(k) if current else None) for k in keep}}
+    return out
 
 
 def copy_calibration(launches: int) -> dict:
@@ -315,6 +342,7 @@ def main() -> int:
         r["bytes"] = int(by)
         r["GB/s"] = round(by / ms / 1e6, 1)
         r["hbm_frac"] = round(by / ms / 1e6 / PEAK_HBM_GBPS, 4)
+        r["profile"] = profile_summary(name)
         if args.no_cpu_baseline:
             r["parity"] = "not checked"
         else:

@@ -96,3 +96,13 @@ def test_oracle_leg_gates_on_parity():
     assert bench.oracle_leg(ln, lspec, linp, _FakeRun(lambda rows: ref(rows) + 0.1))["parity"].startswith("FAIL")
     rows = bench.sample_rows(16384)
     assert rows[0] == 0 and rows[-1] == 16383 and len(rows) > 50 and np.all(np.diff(rows) > 0)
+
+
+def test_every_workload_has_a_profile():
+    """Each workload bench.py times has a committed rocprofv3 summary of its kernels, and
+    bench.py attaches those figures to the workload's result."""
+    for name, _ in bench.SUITE + bench.NEXT:
+        prof = bench.profile_summary(name)
+        assert prof, name
+        for k, rec in prof.items():
+            assert rec["summary"].startswith("profiles/") and k in rec["summary"]
