@@ -115,6 +115,17 @@ constexpr int kEpiThreads = 256;
 // (s_waitcnt) before its thread 0 arrives; the flag is raised only after every arrival
 // has been counted, and slots are read only after the raised flag was seen, so the reads
 // return the published values.
+// In C++ terms the atomics are relaxed, so the language model alone would not order the slot
+// accesses; the ordering is the ISA's, the same properties the compiler's own agent-scope
+// release and acquire sequences rest on. Release there is a write-back of dirty L2 lines,
+// then a wait for every earlier memory operation, then the store: the write-back only serves
+// data written with the default policy, and the slots are written with sc1, so what remains
+// is the wait (s_waitcnt vmcnt(0) here). Acquire there is the load, a wait for it, then an
+// invalidation of non-coherent cached lines: the slots are read with sc1 and never cached
+// non-coherently, so what remains is that the slot loads are issued only after the flag's
+// value has returned (the spin loop's exit depends on it). The flag itself is read before the
+// tile arrives and that load is waited for, so the value it waits to see change cannot
+// already include its own arrival.
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kGroupTiles = 16;
 constexpr int kPolicyCoherent = 16;  // sc1: agent-scope coherence policy of a buffer access
