@@ -412,7 +412,12 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     else load8_n(e.gamma, e.gamma_dtype, f, nv, gam);
   }
 
-  for (int r = tid / TPR; r < nrows; r += RPI) {
+  // When one iteration covers the whole tile (the few-token and fp32 kernels), the bound says so:
+  // with a trip count the compiler cannot bound it strength-reduced the output addresses of every
+  // optional output over several iterations, ~400 instructions ahead of the first barrier.
+  const int r0 = tid / TPR;
+  const int r_end = ROWS_ALLOC <= RPI ? min(nrows, r0 + 1) : nrows;
+  for (int r = r0; r < r_end; r += RPI) {
     const int t = t0 + r;
     const bool t_ok = t < M;
     const bool ok = t_ok && f_ok;
