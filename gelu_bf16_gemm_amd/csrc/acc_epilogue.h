@@ -26,68 +26,6 @@
 
 namespace fusedops {
 
-namespace epi {
-
-// Compile-time description of a kernel instance's epilogue. With kStatic set, the op set,
-// activation and storage types are fixed at compile time; otherwise every choice is read
-// from EpiParams at run time (the generic instance).
-constexpr uint32_t kStatic = 1u << 31;
-constexpr uint32_t kBias = 1u << 0, kZ = 1u << 1, kAux = 1u << 2, kPart = 1u << 3, kGamma = 1u << 4,
-                   kRscale = 1u << 5, kQuant = 1u << 6, kSplit = 1u << 7;
-// RoPE rotations (kRope) have an instance for the fused QKV projection (bias + split) when
-// the head width divides the 256-feature tile; other RoPE op lists run the generic one
-constexpr uint32_t kRope = 1u << 20;
-constexpr uint32_t kXent = 1u << 21;
-constexpr int kActShift = 8, kYShift = 10, kZShift = 12, kAuxShift = 14, kBiasShift = 16, kGammaShift = 18;
-
-constexpr uint32_t config(uint32_t ops, int act, int y_dtype, int z_dtype = FUSEDOPS_BF16,
-                          int aux_dtype = FUSEDOPS_BF16, int bias_dtype = FUSEDOPS_BF16,
-                          int gamma_dtype = FUSEDOPS_BF16) {
-  return kStatic | ops | ((uint32_t)act << kActShift) | ((uint32_t)y_dtype << kYShift) |
-         ((uint32_t)z_dtype << kZShift) | ((uint32_t)aux_dtype << kAuxShift) |
-         ((uint32_t)bias_dtype << kBiasShift) | ((uint32_t)gamma_dtype << kGammaShift);
-}
-
-// The configuration a call's parameters describe (always with kStatic set).
-__host__ __device__ inline uint32_t config_of(const EpiParams& e) {
-  uint32_t ops = 0;
-  if (e.bias) ops |= kBias;
-  if (e.z) ops |= kZ;
-  if (e.aux) ops |= kAux;
-  if (e.partials) ops |= kPart;
-  if (e.gamma) ops |= kGamma;
-  if (e.rscale || e.rms_p) ops |= kRscale;
-  if (e.quant) ops |= kQuant;
-  if (e.n_split) ops |= kSplit;
-  if (e.rope_cs) ops |= kRope;
-  if (e.xent_labels) ops |= kXent;
-  return config(ops, e.act, e.y_dtype, e.z ? e.z_dtype : FUSEDOPS_BF16, e.aux ? e.aux_dtype : FUSEDOPS_BF16,
-                e.bias ? e.bias_dtype : FUSEDOPS_BF16, e.gamma ? e.gamma_dtype : FUSEDOPS_BF16);
-}
-
-template <uint32_t F>
-struct Cfg {
-  static constexpr bool S = (F & kStatic) != 0;
-  const EpiParams& e;
-  __device__ bool bias() const { if constexpr (S) return F & kBias; else return e.bias != nullptr; }
-  __device__ bool z() const { if constexpr (S) return F & kZ; else return e.z != nullptr; }
-  __device__ bool aux() const { if constexpr (S) return F & kAux; else return e.aux != nullptr; }
-  __device__ bool part() const { if constexpr (S) return F & kPart; else return e.partials != nullptr; }
-  __device__ bool gamma() const { if constexpr (S) return F & kGamma; else return e.gamma != nullptr; }
-  __device__ bool rscale() const { if constexpr (S) return F & kRscale; else return e.rscale || e.rms_p; }
-  __device__ bool quant() const { if constexpr (S) return F & kQuant; else return e.quant != 0; }
-  __device__ bool split() const { if constexpr (S) return F & kSplit; else return e.n_split != 0; }
-  __device__ bool xent() const { if constexpr (S) return F & kXent; else return e.xent_labels != nullptr; }
-  __device__ bool rope() const { if constexpr (S) return F & kRope; else return e.rope_cs != nullptr; }
-  __device__ int act() const { if constexpr (S) return (F >> kActShift) & 3; else return e.act; }
-  __device__ int y_dt() const { if constexpr (S) return (F >> kYShift) & 3; else return e.y_dtype; }
-  __device__ int z_dt() const { if constexpr (S) return (F >> kZShift) & 3; else return e.z_dtype; }
-  __device__ int aux_dt() const { if constexpr (S) return (F >> kAuxShift) & 3; else return e.aux_dtype; }
-  __device__ int bias_dt() const { if constexpr (S) return (F >> kBiasShift) & 3; else return e.bias_dtype; }
-  __device__ int gamma_dt() const { if constexpr (S) return (F >> kGammaShift) & 3; else return e.gamma_dtype; }
-};
-
-}  // namespace epi
 
 namespace accepi {
 

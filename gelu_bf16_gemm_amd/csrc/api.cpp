@@ -374,7 +374,7 @@ static int32_t linear_call(const void* X, int64_t ldx, const void* W, int64_t ld
                        : kern == Kernel::SKINNY ? gemm_bf16_skinny_tile_f() : gemm_f32_tile_f(a);
     const void* sym = kern == Kernel::T256 ? gemm_bf16_t256_symbol(a)
                       : kern == Kernel::FP8 ? gemm_fp8_t256_symbol(a.ep)
-                      : kern == Kernel::SKINNY ? gemm_bf16_skinny_symbol() : gemm_f32_symbol(a);
+                      : kern == Kernel::SKINNY ? gemm_bf16_skinny_symbol(a.ep) : gemm_f32_symbol(a);
     const int threads = kern == Kernel::SKINNY ? gemm_bf16_skinny_threads()
                         : kern == Kernel::F32 ? gemm_f32_threads() : 256;
     int dev = 0, cus = 0, per_cu = 0;

@@ -80,6 +80,69 @@ struct GemmArgs {
   EpiParams ep;
 };
 
+namespace epi {
+
+// Compile-time description of a kernel instance's epilogue. With kStatic set, the op set,
+// activation and storage types are fixed at compile time; otherwise every choice is read
+// from EpiParams at run time (the generic instance).
+constexpr uint32_t kStatic = 1u << 31;
+constexpr uint32_t kBias = 1u << 0, kZ = 1u << 1, kAux = 1u << 2, kPart = 1u << 3, kGamma = 1u << 4,
+                   kRscale = 1u << 5, kQuant = 1u << 6, kSplit = 1u << 7;
+// RoPE rotations (kRope) have an instance for the fused QKV projection (bias + split) when
+// the head width divides the 256-feature tile; other RoPE op lists run the generic one
+constexpr uint32_t kRope = 1u << 20;
+constexpr uint32_t kXent = 1u << 21;
+constexpr int kActShift = 8, kYShift = 10, kZShift = 12, kAuxShift = 14, kBiasShift = 16, kGammaShift = 18;
+
+constexpr uint32_t config(uint32_t ops, int act, int y_dtype, int z_dtype = FUSEDOPS_BF16,
+                          int aux_dtype = FUSEDOPS_BF16, int bias_dtype = FUSEDOPS_BF16,
+                          int gamma_dtype = FUSEDOPS_BF16) {
+  return kStatic | ops | ((uint32_t)act << kActShift) | ((uint32_t)y_dtype << kYShift) |
+         ((uint32_t)z_dtype << kZShift) | ((uint32_t)aux_dtype << kAuxShift) |
+         ((uint32_t)bias_dtype << kBiasShift) | ((uint32_t)gamma_dtype << kGammaShift);
+}
+
+// The configuration a call's parameters describe (always with kStatic set).
+__host__ __device__ inline uint32_t config_of(const EpiParams& e) {
+  uint32_t ops = 0;
+  if (e.bias) ops |= kBias;
+  if (e.z) ops |= kZ;
+  if (e.aux) ops |= kAux;
+  if (e.partials) ops |= kPart;
+  if (e.gamma) ops |= kGamma;
+  if (e.rscale || e.rms_p) ops |= kRscale;
+  if (e.quant) ops |= kQuant;
+  if (e.n_split) ops |= kSplit;
+  if (e.rope_cs) ops |= kRope;
+  if (e.xent_labels) ops |= kXent;
+  return config(ops, e.act, e.y_dtype, e.z ? e.z_dtype : FUSEDOPS_BF16, e.aux ? e.aux_dtype : FUSEDOPS_BF16,
+                e.bias ? e.bias_dtype : FUSEDOPS_BF16, e.gamma ? e.gamma_dtype : FUSEDOPS_BF16);
+}
+
+template <uint32_t F>
+struct Cfg {
+  static constexpr bool S = (F & kStatic) != 0;
+  const EpiParams& e;
+  __device__ bool bias() const { if constexpr (S) return F & kBias; else return e.bias != nullptr; }
+  __device__ bool z() const { if constexpr (S) return F & kZ; else return e.z != nullptr; }
+  __device__ bool aux() const { if constexpr (S) return F & kAux; else return e.aux != nullptr; }
+  __device__ bool part() const { if constexpr (S) return F & kPart; else return e.partials != nullptr; }
+  __device__ bool gamma() const { if constexpr (S) return F & kGamma; else return e.gamma != nullptr; }
+  __device__ bool rscale() const { if constexpr (S) return F & kRscale; else return e.rscale || e.rms_p; }
+  __device__ bool quant() const { if constexpr (S) return F & kQuant; else return e.quant != 0; }
+  __device__ bool split() const { if constexpr (S) return F & kSplit; else return e.n_split != 0; }
+  __device__ bool xent() const { if constexpr (S) return F & kXent; else return e.xent_labels != nullptr; }
+  __device__ bool rope() const { if constexpr (S) return F & kRope; else return e.rope_cs != nullptr; }
+  __device__ int act() const { if constexpr (S) return (F >> kActShift) & 3; else return e.act; }
+  __device__ int y_dt() const { if constexpr (S) return (F >> kYShift) & 3; else return e.y_dtype; }
+  __device__ int z_dt() const { if constexpr (S) return (F >> kZShift) & 3; else return e.z_dtype; }
+  __device__ int aux_dt() const { if constexpr (S) return (F >> kAuxShift) & 3; else return e.aux_dtype; }
+  __device__ int bias_dt() const { if constexpr (S) return (F >> kBiasShift) & 3; else return e.bias_dtype; }
+  __device__ int gamma_dt() const { if constexpr (S) return (F >> kGammaShift) & 3; else return e.gamma_dtype; }
+};
+
+}  // namespace epi
+
 constexpr int kEpiThreads = 256;
 
 // ---------------------------------------------------------------------------
@@ -376,13 +439,14 @@ enum EpiMode {
 // accumulator of token t0 + r and feature f0 + c. NSRC tiles (each ROWS_ALLOC x COLS) are
 // summed element-wise first, in order (used to merge split-K partial sums). Every thread
 // of the block must call this (it contains wave-wide shuffles but no barriers).
-template <int COLS, int NSRC, int ROWS_ALLOC>
+template <int COLS, int NSRC, int ROWS_ALLOC, uint32_t F = 0>
 __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* tile, int t0,
                                               int nrows, int f0, int ft, const float* amax_rows, int mode) {
   constexpr int TPR = COLS / 8;            // threads per row
   constexpr int RPI = kEpiThreads / TPR;   // rows per iteration
   static_assert(TPR <= 64 && 64 % TPR == 0, "a row's threads must sit in one wave");
   const EpiParams& e = a.ep;
+  const epi::Cfg<F> cfg{e};  // F = 0: every choice read at run time
   const int M = a.M, N = a.N;
   const int tid = threadIdx.x;
   const int g = tid % TPR;
@@ -393,23 +457,25 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
   // whose width is not a multiple of 8 (the rest read as 0 and are neither stored nor reduced)
   const int nv = f_ok ? min(8, N - f) : 0;
   const bool full = nv == 8;
-  const bool swiglu = e.act == ACT_SWIGLU;
+  const int act = cfg.act();
+  const bool swiglu = act == ACT_SWIGLU;
   const bool side = mode != EPI_QUANT;
-  const int zb = e.z_dtype == FUSEDOPS_F32 ? 4 : 2;
-  const int ab = e.aux_dtype == FUSEDOPS_F32 ? 4 : 2;
-  const int yb = e.y_dtype == FUSEDOPS_F32 ? 4 : (e.y_dtype == FUSEDOPS_F8E4M3 ? 1 : 2);
+  const int zdt = cfg.z_dt(), adt = cfg.aux_dt(), ydt = cfg.y_dt();
+  const int zb = zdt == FUSEDOPS_F32 ? 4 : 2;
+  const int ab = adt == FUSEDOPS_F32 ? 4 : 2;
+  const int yb = ydt == FUSEDOPS_F32 ? 4 : (ydt == FUSEDOPS_F8E4M3 ? 1 : 2);
 
   // per-feature vectors, loaded once per pass
   float bias[8], gam[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) { bias[i] = 0.f; gam[i] = 1.f; }
-  if (e.bias && f_ok) {
-    if (full) load8(e.bias, e.bias_dtype, f, bias);
-    else load8_n(e.bias, e.bias_dtype, f, nv, bias);
+  if (cfg.bias() && f_ok) {
+    if (full) load8(e.bias, cfg.bias_dt(), f, bias);
+    else load8_n(e.bias, cfg.bias_dt(), f, nv, bias);
   }
-  if (e.gamma && f_ok) {
-    if (full) load8(e.gamma, e.gamma_dtype, f, gam);
-    else load8_n(e.gamma, e.gamma_dtype, f, nv, gam);
+  if (cfg.gamma() && f_ok) {
+    if (full) load8(e.gamma, cfg.gamma_dt(), f, gam);
+    else load8_n(e.gamma, cfg.gamma_dt(), f, nv, gam);
   }
 
   // When one iteration covers the whole tile (the few-token and fp32 kernels), the bound says so:
@@ -439,20 +505,20 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     // bias, residual
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] += bias[i];
-    if (e.z && ok) {
+    if (cfg.z() && ok) {
       float z[8];
-      if (full) load8(static_cast<const char*>(e.z) + (int64_t)t * e.ldz * zb, e.z_dtype, f, z);
-      else load8_n(static_cast<const char*>(e.z) + (int64_t)t * e.ldz * zb, e.z_dtype, f, nv, z);
+      if (full) load8(static_cast<const char*>(e.z) + (int64_t)t * e.ldz * zb, zdt, f, z);
+      else load8_n(static_cast<const char*>(e.z) + (int64_t)t * e.ldz * zb, zdt, f, nv, z);
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] += z[i];
     }
     // store-aux (h1) and its row sum-of-squares partials over 128-column chunks
-    if (side && e.aux && ok) {
+    if (side && cfg.aux() && ok) {
       char* arow = static_cast<char*>(e.aux) + (int64_t)t * e.ld_aux * ab;
-      if (full) store8(arow, e.aux_dtype, f, v);
-      else store_n<8>(arow, e.aux_dtype, f, nv, v);
+      if (full) store8(arow, adt, f, v);
+      else store_n<8>(arow, adt, f, nv, v);
     }
-    if (COLS >= 128 && e.partials) {
+    if (COLS >= 128 && cfg.part()) {
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) s += v[i] * v[i];
@@ -464,23 +530,23 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     // column scale, row scale
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] *= gam[i];
-    if (e.rscale || e.rms_p) {
+    if (cfg.rscale()) {
       const float rs = t_ok ? row_scale_of(e, t) : 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] *= rs;
     }
     // activation; SwiGLU leaves its 4 outputs in v[0..3]
-    if (e.act == ACT_GELU_ERF) {
+    if (act == ACT_GELU_ERF) {
       // fp32 outputs keep fp32 relative accuracy in the negative tail; 16-bit and E4M3
       // outputs take the one-exp2 form, whose error is far below their rounding
-      if (e.y_dtype == FUSEDOPS_F32) {
+      if (ydt == FUSEDOPS_F32) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = gelu_erf_precise_f32(v[i]);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = gelu_erf_f32(v[i]);
       }
-    } else if (e.act == ACT_GELU_TANH) {
+    } else if (act == ACT_GELU_TANH) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = gelu_tanh_f32(v[i]);
     } else if (swiglu) {
@@ -490,7 +556,7 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
       for (int j = 4; j < 8; ++j) v[j] = 0.f;
     }
     // RoPE on adjacent pairs: the thread's 8 columns lie in one head (d is a multiple of 8)
-    if (e.rope_cs && ok && f < e.rope_cols) {
+    if (cfg.rope() && ok && f < e.rope_cols) {
       const float* cs = e.rope_cs + (int64_t)t * e.rope_ld + (f % e.rope_d);
       const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
       const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
@@ -504,7 +570,7 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     }
     // cross-entropy statistics: (max, sum of e^(y - max)) of each 64-column chunk, merged over
     // the chunk's 8 threads, and y at the row's label (tile-local index selection)
-    if (e.xent_labels) {
+    if (cfg.xent()) {
       constexpr float kLog2e = 1.4426950408889634f;
       float m = -INFINITY, sx = 0.f;
       if (ok) {
@@ -540,23 +606,23 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
     const int fo = swiglu ? f / 2 : f;  // output column of v[0]
 
     if (mode == EPI_STORE) {
-      if (!ok || (!e.y && !e.n_split)) continue;  // no Y: the logits are not stored (XENT)
+      if (!ok || (!e.y && !cfg.split())) continue;  // no Y: the logits are not stored (XENT)
       if (swiglu) {
         char* yrow = static_cast<char*>(e.y) + (int64_t)t * e.ldy * yb;
         if (full) {
-          store4(yrow, e.y_dtype, fo, f32x4{v[0], v[1], v[2], v[3]});
+          store4(yrow, ydt, fo, f32x4{v[0], v[1], v[2], v[3]});
         } else {
           const float o4[4] = {v[0], v[1], v[2], v[3]};
-          store_n<4>(yrow, e.y_dtype, fo, nv / 2, o4);   // N is even with SwiGLU
+          store_n<4>(yrow, ydt, fo, nv / 2, o4);   // N is even with SwiGLU
         }
-      } else if (e.n_split) {
+      } else if (cfg.split()) {
         const int seg = (int)(f / e.split_w);
         void* base = seg == 0 ? e.yv0 : (seg == 1 ? e.yv1 : e.yv2);
-        store8(static_cast<char*>(base) + (int64_t)t * e.ldv * yb, e.y_dtype, f - (int64_t)seg * e.split_w, v);
+        store8(static_cast<char*>(base) + (int64_t)t * e.ldv * yb, ydt, f - (int64_t)seg * e.split_w, v);
       } else {
         char* yrow = static_cast<char*>(e.y) + (int64_t)t * e.ldy * yb;
-        if (full) store8(yrow, e.y_dtype, f, v);
-        else store_n<8>(yrow, e.y_dtype, f, nv, v);
+        if (full) store8(yrow, ydt, f, v);
+        else store_n<8>(yrow, ydt, f, nv, v);
       }
     } else if (mode == EPI_AMAX) {
       float m = 0.f;
@@ -599,12 +665,13 @@ __device__ __forceinline__ void epilogue_pass(const GemmArgs& a, const float* ti
 // is (t0, f0) and each pass covers ROWS tokens (`nrows_total` valid tokens in the tile).
 // For FP8 row quantisation the chain runs twice: first to publish the row absmax, then,
 // after every column tile of the token block has done so, to quantise.
-template <int COLS, int NSRC, int ROWS, int PASSES, typename StageFn>
+template <int COLS, int NSRC, int ROWS, int PASSES, uint32_t F = 0, typename StageFn>
 __device__ __forceinline__ void run_staged_epilogue(const GemmArgs& a, float* tile, int t0, int f0,
                                                     int nrows_total, int ft, int* lds_slot,
                                                     float* lds_amax, StageFn&& stage) {
   const EpiParams& e = a.ep;
-  const int rounds = e.quant ? 2 : 1;
+  const epi::Cfg<F> cfg{e};
+  const int rounds = cfg.quant() ? 2 : 1;
   // rolled loops: one inlined copy of the chain serves every round and pass
 #pragma clang loop unroll(disable)
   for (int round = 0; round < rounds; ++round) {
@@ -612,7 +679,7 @@ __device__ __forceinline__ void run_staged_epilogue(const GemmArgs& a, float* ti
       // every column tile of the row block publishes: this tile's rows' maxima, once
       rendezvous_row_amax<ROWS * PASSES>(e, ft, a.tiles_f, t0, nrows_total, lds_amax, lds_slot);
     }
-    const int mode = e.quant ? (round == 0 ? EPI_AMAX : EPI_QUANT) : EPI_STORE;
+    const int mode = cfg.quant() ? (round == 0 ? EPI_AMAX : EPI_QUANT) : EPI_STORE;
 #pragma clang loop unroll(disable)
     for (int p = 0; p < PASSES; ++p) {
       const int rows = min(ROWS, nrows_total - p * ROWS);
@@ -620,7 +687,7 @@ __device__ __forceinline__ void run_staged_epilogue(const GemmArgs& a, float* ti
       __syncthreads();
       stage(p, tile);
       __syncthreads();
-      epilogue_pass<COLS, NSRC, ROWS>(a, tile, t0 + p * ROWS, rows, f0, ft, lds_amax + p * ROWS, mode);
+      epilogue_pass<COLS, NSRC, ROWS, F>(a, tile, t0 + p * ROWS, rows, f0, ft, lds_amax + p * ROWS, mode);
     }
   }
 }

@@ -33,6 +33,9 @@ constexpr int kWBytes = BF * kRowBytes;      // 32 KB of W per stage
 constexpr int kBufBytes = (BF + BT) * kRowBytes;  // 48 KB per stage buffer: W rows, then X rows
 constexpr int DR = 2;                        // stages in flight in registers
 
+// F: the epilogue configuration (epi::config) the instance is compiled for, or 0 for the generic
+// instance, which reads every choice at run time.
+template <uint32_t F>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_skinny_kernel(GemmArgs a) {
   // two stage buffers; afterwards they hold the 4 partial 32 x 64 fp32 tiles (32 KB) the
   // epilogue sums
@@ -143,10 +146,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_skinny_kernel(GemmArgs 
   }
   __syncthreads();
 
-  run_staged_epilogue<BF, 4, BT, 1>(a, reinterpret_cast<float*>(lds), t0, f0, min(BT, a.M - t0), ft, slot,
+  run_staged_epilogue<BF, 4, BT, 1, F>(a, reinterpret_cast<float*>(lds), t0, f0, min(BT, a.M - t0), ft, slot,
                                     s_amax, [&](int, float* tile) {
                                       stage_block<BF>(tile + kq * BT * BF, acc, fb * 32, 0);
                                     });
+}
+
+// The decode layer's epilogue (SwiGLU, then FP8 rows) has an instance of its own; any other op
+// list runs the generic one.
+constexpr uint32_t kCfgSwigluFp8 = epi::config(epi::kQuant, ACT_SWIGLU, FUSEDOPS_F8E4M3);
+
+const void* skinny_kernel_for(const EpiParams& e) {
+  if (epi::config_of(e) == kCfgSwigluFp8)
+    return reinterpret_cast<const void*>(&gemm_bf16_skinny_kernel<kCfgSwigluFp8>);
+  return reinterpret_cast<const void*>(&gemm_bf16_skinny_kernel<0>);
 }
 
 }  // namespace
@@ -155,13 +168,12 @@ hipError_t launch_gemm_bf16_skinny(GemmArgs a, hipStream_t stream) {
   a.tiles_t = (a.M + BT - 1) / BT;
   a.tiles_f = (a.N + BF - 1) / BF;
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_bf16_skinny_kernel), dim3(a.tiles_t * a.tiles_f),
-                         dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(skinny_kernel_for(a.ep), dim3(a.tiles_t * a.tiles_f), dim3(kThreads), args, 0, stream);
 }
 
 int gemm_bf16_skinny_tile_t() { return BT; }
 int gemm_bf16_skinny_tile_f() { return BF; }
 int gemm_bf16_skinny_threads() { return kThreads; }
-const void* gemm_bf16_skinny_symbol() { return reinterpret_cast<const void*>(&gemm_bf16_skinny_kernel); }
+const void* gemm_bf16_skinny_symbol(const EpiParams& e) { return skinny_kernel_for(e); }
 
 }  // namespace fusedops

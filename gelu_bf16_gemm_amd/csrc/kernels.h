@@ -29,7 +29,7 @@ hipError_t launch_gemm_bf16_skinny(GemmArgs a, hipStream_t stream);
 int gemm_bf16_skinny_tile_t();
 int gemm_bf16_skinny_tile_f();
 int gemm_bf16_skinny_threads();
-const void* gemm_bf16_skinny_symbol();
+const void* gemm_bf16_skinny_symbol(const EpiParams& e);
 
 // fp32 GEMM + epilogue (v_mfma_f32_32x32x2_f32), 32-token x 64-feature tiles (128 features
 // when the op list writes RMSNorm row partials), K split over the 8 waves of a workgroup.

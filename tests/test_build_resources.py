@@ -32,7 +32,7 @@ T256_BUDGET = {"generic": (108, 0), "bias+gelu_erf": (24, 36), "bias+split": (36
                "rowscale+swiglu": (28, 36), "xent": (572, 252), "bias+split+rope": (56, 120)}
 # the other GEMM kernels, by instance (E4M3 inputs: epilogue configuration id; fp32: token tile)
 OTHER_BUDGET = {"gemm_fp8_t256_kernelILj2147833089E": 36, "gemm_fp8_t256_kernelILj2147832834E": 100,
-                "gemm_fp8_t256_kernelILj0E": 44, "gemm_bf16_skinny_kernelE": 0,
+                "gemm_fp8_t256_kernelILj0E": 44, "gemm_bf16_skinny_kernelI": 0,
                 "gemm_f32_kernelILi128E": 0, "gemm_f32_kernelILi64E": 0}
 # resident waves per SIMD the launch configuration of each kernel relies on
 OCCUPANCY = {"gemm_bf16_t256_kernel": 1, "gemm_fp8_t256_kernel": 1, "gemm_bf16_skinny_kernel": 2}
