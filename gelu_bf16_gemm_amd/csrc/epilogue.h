@@ -64,11 +64,23 @@ struct EpiParams {
 
 // The row scale of token t: ROW_SCALE's r[t], or ROW_RMS's r computed from the token's row
 // partials with the formula of the finalize kernel, 1 / sqrt(sum / width + eps).
+// The partials are loaded 16 at a time with all loads in flight before the first is added (a
+// plain loop loaded, waited and added one at a time: 16 round trips per tile at width 2048, each
+// wait also covering every other load and store in flight); they are added in index order.
 __device__ inline float row_scale_of(const EpiParams& e, int t) {
   if (e.rscale) return e.rscale[t];
   const float* p = e.rms_p + (int64_t)t * e.rms_ldp;
+  const int T = e.rms_T;
   float s = 0.f;
-  for (int i = 0; i < e.rms_T; ++i) s += p[i];
+  int i = 0;
+  for (; i + 16 <= T; i += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = p[i + j];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += v[j];
+  }
+  for (; i < T; ++i) s += p[i];
   return 1.0f / sqrtf(s / (float)e.rms_n + e.rms_eps);
 }
 
