@@ -185,9 +185,7 @@ __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int r
   }
 }
 
-}  // namespace accepi
-
-// Keep an updated accumulator block in AGPRs. The chain visits all 16 blocks per step and keeps
+// Keep an updated accumulator block in AGPRs (the residual seed and the epilogue). The chain visits all 16 blocks per step and keeps
 // every block between steps; left to itself the compiler holds the updated values in VGPRs,
 // runs out of them and spills to scratch, each reload then waiting with vmcnt(0) for every
 // load and store in flight. AGPRs are where the MFMAs left the blocks, and there is room.
@@ -198,10 +196,111 @@ __device__ __forceinline__ void to_agpr(f32x16& v) {
   if constexpr ((F & epi::kStatic) != 0 && (F & epi::kQuant) == 0) asm volatile("" : "+a"(v));
 }
 
+// Copy pass p (rows p * R .. p * R + R - 1 of the tile, R = 256 / passes) of the residual
+// z into LDS in the staged-tile layout by DMA (each wave instruction fills 1 KB: lane i lands
+// at position 16 i, so it fetches the chunk whose swizzled position that is), all
+// instructions in flight at once, then wait until every wave's copies have landed. Rows past
+// M and columns past N read as zero; a pass with no valid rows is zero-filled. The caller
+// has made `lds` free (a barrier after its last reads).
+template <class Cfg>
+__device__ __forceinline__ void z_pass_to_lds(const EpiParams& e, const Cfg& cfg, uint8_t* lds, int t0, int f0,
+                                              int M, int N, int p, int R, int C) {
+  const int es = dt_bytes(cfg.z_dt());
+  const int cshift = __builtin_ctz(C);
+  const int m = (C < 32 ? C : 32) - 1;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane_u = threadIdx.x & 63;
+  const int rows = min(R, M - t0 - p * R);  // valid rows of this pass (>= 1 for p = 0)
+  if (rows > 0) {
+    // The range ends at the 16-byte chunk boundary after the last valid column: a load that
+    // crosses the end of the range reads as zero as a whole, which would drop the valid
+    // columns of a chunk that N cuts through. The chunk lies inside its row's storage (the
+    // leading dimension keeps rows 16-byte aligned); its columns past N are the caller's.
+    const uint8_t* zb = static_cast<const uint8_t*>(e.z) + ((int64_t)(t0 + p * R) * e.ldz + f0) * es;
+    const int zcols = (min(kTileCols, N - f0) + 16 / es - 1) / (16 / es) * (16 / es);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zb, (uint32_t)(((int64_t)(rows - 1) * e.ldz + zcols) * es));
+#pragma unroll 8
+    for (int j = 0; j < R * C / kEpiThreads; ++j) {
+      const int id = j * kEpiThreads + wave * 64 + lane_u;
+      const int r = id >> cshift, pos = id & (C - 1);
+      const int c = pos ^ (r & m);
+      const uint32_t oob = (uint32_t)(f0 + c * 16 / es >= N) << 31;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(lds + (j * kEpiThreads + wave * 64) * 16), 16,
+                                               ((uint32_t)(r * e.ldz * es + c * 16)) | oob, 0, 0, kNonTemporal);
+    }
+  } else {
+    for (int id = threadIdx.x; id < R * C; id += kEpiThreads)
+      *reinterpret_cast<u32x4*>(lds + id * 16) = u32x4{0, 0, 0, 0};
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+  lds_barrier();
+}
+
+// Whether a configuration's accumulators start from the residual (see seed_residual).
+template <uint32_t F>
+constexpr bool seeds_residual() {
+  return (F & epi::kStatic) != 0 && (F & epi::kZ) != 0;
+}
+
+// Start a tile's accumulators from its residual rows plus the bias, acc = z + b, before the
+// mainloop: the MFMAs then accumulate the product on top, and the epilogue has neither the
+// residual copy nor the add ([Epilogue] §模式A: h1 = residual + the GEMM output, computed here in
+// the other association, fp32 throughout). At the start of a tile no accumulator is live, so
+// the per-group reads need no registers the epilogue would have to give up. For tiles whose
+// columns are all inside N (the LDS-DMA mainloop's condition, N % 256 == 0). `lds` is 128 KB
+// of LDS no wave is using; `svec` holds the bias when the configuration has one; on return
+// `lds` is free again.
+template <uint32_t F>
+__device__ __forceinline__ void seed_residual(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, const float* svec,
+                                              int t0, int f0) {
+  const EpiParams& e = a.ep;
+  const epi::Cfg<F> cfg{e};
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wf = wave >> 1, wt = wave & 1;
+  const int hb = lane >> 5, tl = lane & 31;
+  const int zdt = cfg.z_dt();
+  const int es = dt_bytes(zdt);
+  const int C = kTileCols * es / 16;
+  constexpr int passes = (kTileRows * kTileCols * (((F >> epi::kZShift) & 3) == FUSEDOPS_F32 ? 4 : 2)) > kStageBytes ? 2 : 1;
+  constexpr int R = kTileRows / passes;
+#pragma unroll
+  for (int p = 0; p < passes; ++p) {
+    if (p > 0) lds_barrier();  // every wave has read the previous pass
+    z_pass_to_lds(e, cfg, lds, t0, f0, a.M, a.N, p, R, C);
+    if (passes == 1 || wt == p) {
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        f32x4 b[4] = {};
+        if (cfg.bias()) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) b[q] = *reinterpret_cast<const f32x4*>(svec + wf * 128 + fb * 32 + q * 8 + hb * 4);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const int r = wt * 128 + tb * 32 + tl - p * R;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 z = lds_get4(lds, st_off(r, (wf * 128 + fb * 32 + q * 8 + hb * 4) * es, C), zdt);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[fb][tb][4 * q + j] = z[j] + b[q][j];
+          }
+          to_agpr<F>(acc[fb][tb]);
+        }
+      }
+    }
+  }
+  lds_barrier();  // every wave has read its groups: `lds` is free
+}
+
+}  // namespace accepi
+
 // Run the whole epilogue of one 256 x 256 tile whose accumulators are in `acc` (the
 // layout above). `lds` is at least 128 KB of LDS that the mainloop no longer uses and
 // `svec` the tile's vectors (VecPrefetch); every thread of the workgroup must call this.
-template <uint32_t F>
+// kSeeded: the accumulators started from the residual and bias (seed_residual), so neither is
+// added here.
+template <uint32_t F, bool kSeeded = false>
 __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, const float* svec,
                                              int t0, int f0, int ft, int* slot) {
   using namespace accepi;
@@ -388,7 +487,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
   }
 
   // ---- pre-activation h1 = acc + bias + residual, in place
-  if (cfg.bias()) {
+  if (cfg.bias() && !kSeeded) {
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
       const f32x16 b = feat(0, fb);
@@ -399,47 +498,18 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
       }
     }
   }
-  if (cfg.z()) {
-    // The residual rows are copied into the staged-tile layout by LDS DMA (each wave
-    // instruction fills 1 KB: lane i lands at position 16 i, so it fetches the chunk whose
-    // swizzled position that is), all instructions in flight at once; then per-group reads.
-    // Rows past M and columns past N read as zero (out-of-range buffer offsets).
+  if (cfg.z() && !kSeeded) {
+    // The residual rows are copied into the staged-tile layout (z_pass_to_lds), then read
+    // back per group.
     const int zdt = cfg.z_dt();
     const int es = dt_bytes(zdt);
     const int C = kTileCols * es / 16;
     const int passes = kTileRows * kTileCols * es > kStageBytes ? 2 : 1;
     const int R = kTileRows / passes;
-    const int cshift = __builtin_ctz(C);
-    const int m = (C < 32 ? C : 32) - 1;
-    const int lane_u = threadIdx.x & 63;
 #pragma clang loop unroll(disable)
     for (int p = 0; p < passes; ++p) {
-      const int rows = min(R, M - t0 - p * R);  // valid rows of this pass (>= 1 for p = 0)
       lds_barrier();
-      if (rows > 0) {
-        // The range ends at the 16-byte chunk boundary after the last valid column: a load that
-        // crosses the end of the range reads as zero as a whole, which would drop the valid
-        // columns of a chunk that N cuts through. The chunk lies inside its row's storage (the
-        // leading dimension keeps rows 16-byte aligned); its columns past N are zeroed below.
-        const uint8_t* zb = static_cast<const uint8_t*>(e.z) + ((int64_t)(t0 + p * R) * e.ldz + f0) * es;
-        const int zcols = (min(kTileCols, N - f0) + 16 / es - 1) / (16 / es) * (16 / es);
-        const __amdgpu_buffer_rsrc_t rz = make_rsrc(zb, (uint32_t)(((int64_t)(rows - 1) * e.ldz + zcols) * es));
-#pragma unroll 8
-        for (int j = 0; j < R * C / kEpiThreads; ++j) {
-          const int id = j * kEpiThreads + wave * 64 + lane_u;
-          const int r = id >> cshift, pos = id & (C - 1);
-          const int c = pos ^ (r & m);
-          const uint32_t oob = (uint32_t)(f0 + c * 16 / es >= N) << 31;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(lds + (j * kEpiThreads + wave * 64) * 16), 16,
-                                                   ((uint32_t)(r * e.ldz * es + c * 16)) | oob, 0, 0, kNonTemporal);
-        }
-      } else {
-        // no valid rows: zero this pass's tile
-        for (int id = threadIdx.x; id < R * C; id += kEpiThreads)
-          *reinterpret_cast<u32x4*>(lds + id * 16) = u32x4{0, 0, 0, 0};
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
-      lds_barrier();
+      z_pass_to_lds(e, cfg, lds, t0, f0, M, N, p, R, C);
       if (passes == 1 || wt == p) {
         // a 16-byte chunk that N cuts through was loaded whole: in the wave whose features reach
         // past N (uniform), its columns past N are zeroed so they add nothing to h1 and to the

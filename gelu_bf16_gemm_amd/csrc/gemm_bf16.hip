@@ -259,11 +259,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uin
   accepi::VecPrefetch vp;
   if constexpr ((F & epi::kStatic) != 0) vp.load<F>(a.ep, t0, f0, a.M, a.N);
 
+  // A residual configuration on the LDS-DMA path starts its accumulators from z (+ bias);
+  // every other tile starts from zero.
+  constexpr bool kSeed = kDma && accepi::seeds_residual<F>();
   f32x16 acc[4][4];
+  if constexpr (kSeed) {
+    if constexpr ((F & epi::kBias) != 0) vp.store(svec);  // seed_residual reads the bias
+    accepi::seed_residual<F>(a, acc, smem, svec, t0, f0);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  }
 
   if constexpr (kDma) {
     mainloop_dma<F>(a, smem, svec, vp, acc, t0, f0);
@@ -419,7 +427,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uin
   if constexpr ((F & epi::kStatic) != 0) {
     // Epilogue on the accumulators in place; the mainloop's LDS buffers (128 KB) stage
     // the finished values for coalesced stores.
-    acc_epilogue<F>(a, acc, smem, svec, t0, f0, ft, slot);
+    acc_epilogue<F, kSeed>(a, acc, smem, svec, t0, f0, ft, slot);
   } else {
     // Any other op list: the fp32 tile is staged through LDS in two 128-token passes
     // (128 KB each; pass p takes the accumulators of the waves with wt == p) and the
