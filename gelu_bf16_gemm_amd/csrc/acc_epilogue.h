@@ -236,10 +236,16 @@ __device__ __forceinline__ void z_pass_to_lds(const EpiParams& e, const Cfg& cfg
   lds_barrier();
 }
 
-// Whether a configuration's accumulators start from the residual (see seed_residual).
+// Whether a configuration's accumulators start from the residual (see seed_residual), or,
+// with no residual, from the bias (written by the LDS-DMA mainloop before its first MFMA).
 template <uint32_t F>
 constexpr bool seeds_residual() {
   return (F & epi::kStatic) != 0 && (F & epi::kZ) != 0;
+}
+// (Not with RoPE: that instance measured 660 B of spills per lane seeded against 56 unseeded.)
+template <uint32_t F>
+constexpr bool seeds_bias() {
+  return (F & epi::kStatic) != 0 && (F & epi::kBias) != 0 && (F & epi::kZ) == 0 && (F & epi::kRope) == 0;
 }
 
 // Start a tile's accumulators from its residual rows plus the bias, acc = z + b, before the
@@ -298,8 +304,8 @@ __device__ __forceinline__ void seed_residual(const GemmArgs& a, f32x16 (&acc)[4
 // Run the whole epilogue of one 256 x 256 tile whose accumulators are in `acc` (the
 // layout above). `lds` is at least 128 KB of LDS that the mainloop no longer uses and
 // `svec` the tile's vectors (VecPrefetch); every thread of the workgroup must call this.
-// kSeeded: the accumulators started from the residual and bias (seed_residual), so neither is
-// added here.
+// kSeeded: the accumulators started from the residual and the bias (seed_residual, or the bias
+// alone when there is no residual), so neither is added here.
 template <uint32_t F, bool kSeeded = false>
 __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, const float* svec,
                                              int t0, int f0, int ft, int* slot) {
@@ -409,7 +415,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     // token's table row (d divides the 256-feature tile, so f mod d = local feature mod d).
     // Groups at or past rope_cols (V under a Q/K/V split) stay as computed; that test depends
     // only on the feature, so it is uniform in a wave. Table rows past M read as zero.
-    if (cfg.bias()) {
+    if (cfg.bias() && !kSeeded) {
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
         const f32x16 b = feat(0, fb);
@@ -475,12 +481,12 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     int fb_loaded = -1;
     emit(ydt, pairs, dy, [&](int fb, int tb) __attribute__((always_inline)) {
       if (fb != fb_loaded) {
-        if (cfg.bias()) b = feat(0, fb);
+        if (cfg.bias() && !kSeeded) b = feat(0, fb);
         if (cfg.gamma()) g = feat(1, fb);
         fb_loaded = fb;
       }
       f32x16 v = acc[fb][tb];
-      if (cfg.bias()) v += b;
+      if (cfg.bias() && !kSeeded) v += b;
       return post(v, g, tb);
     });
     return;

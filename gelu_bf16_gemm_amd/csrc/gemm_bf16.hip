@@ -88,7 +88,10 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 // barrier together, and DMAs issued back to back would queue at the CU's address unit while
 // the matrix core idles. Each barrier waits for exactly the DMAs the next region reads; the
 // counts follow from this fixed issue order, which the prologue reproduces.
-template <uint32_t F>
+//
+// kBiasStart: the accumulators start from the tile's bias (written here, once the prologue's
+// first barrier has made the LDS copy of the vectors visible) instead of from zero.
+template <uint32_t F, bool kBiasStart>
 __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, float* svec,
                                              const accepi::VecPrefetch& vp, f32x16 (&acc)[4][4], int t0, int f0) {
   constexpr int kBuf = 2 * kTileBytes;  // one stage: W tile then X tile
@@ -226,6 +229,23 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   dma_w(1, 0); dma_w(1, 1); dma_x(1, 1);
   if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
   dma_wait_barrier<16>();  // X and W blocks 0-1 of step 0
+  if constexpr (kBiasStart) {
+    // register 4q + j of block (fb, tb) holds feature wf*128 + fb*32 + 8q + 4*(lane/32) + j
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(svec + wf * 128 + fb * 32 + q * 8 + (lane >> 5) * 4);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[fb][tb][4 * q + j] = b[j];
+      }
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) accepi::to_agpr<F>(acc[fb][tb]);
+  }
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -259,13 +279,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uin
   accepi::VecPrefetch vp;
   if constexpr ((F & epi::kStatic) != 0) vp.load<F>(a.ep, t0, f0, a.M, a.N);
 
-  // A residual configuration on the LDS-DMA path starts its accumulators from z (+ bias);
-  // every other tile starts from zero.
-  constexpr bool kSeed = kDma && accepi::seeds_residual<F>();
+  // On the LDS-DMA path a static configuration's accumulators start from its residual and
+  // bias (seed_residual) or, without a residual, from its bias (in mainloop_dma): the MFMAs
+  // accumulate the product on top and the epilogue adds neither. Every other tile starts from
+  // zero.
+  constexpr bool kSeed = kDma && (accepi::seeds_residual<F>() || accepi::seeds_bias<F>());
   f32x16 acc[4][4];
-  if constexpr (kSeed) {
+  if constexpr (kDma && accepi::seeds_residual<F>()) {
     if constexpr ((F & epi::kBias) != 0) vp.store(svec);  // seed_residual reads the bias
     accepi::seed_residual<F>(a, acc, smem, svec, t0, f0);
+  } else if constexpr (kSeed) {
+    // written in mainloop_dma
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -274,7 +298,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uin
   }
 
   if constexpr (kDma) {
-    mainloop_dma<F>(a, smem, svec, vp, acc, t0, f0);
+    mainloop_dma<F, kSeed && !accepi::seeds_residual<F>()>(a, smem, svec, vp, acc, t0, f0);
   } else {
     // Buffer resources over this tile's rows: rows past M / N read as zero.
     const int w_rows = min(BF, a.N - f0), x_rows = min(BT, a.M - t0);

@@ -27,7 +27,7 @@ CFG = {0: "generic", 2147833089: "bias+gelu_erf", 2147832961: "bias+split", 2147
        2147833600: "swiglu", 2147835712: "swiglu+fp8", 2147833632: "rowscale+swiglu", 2149929984: "xent",
        2148881537: "bias+split+rope"}
 # scratch bytes per lane allowed outside the K loop: (LDS-DMA mainloop, register-staged mainloop)
-T256_BUDGET = {"generic": (108, 0), "bias+gelu_erf": (24, 36), "bias+split": (36, 60),
+T256_BUDGET = {"generic": (108, 0), "bias+gelu_erf": (0, 36), "bias+split": (0, 60),
                "residual+aux+rms+gamma": (188, 136), "swiglu": (24, 52), "swiglu+fp8": (164, 204),
                "rowscale+swiglu": (28, 36), "xent": (572, 252), "bias+split+rope": (56, 120)}
 # the other GEMM kernels, by instance (E4M3 inputs: epilogue configuration id; fp32: token tile)
