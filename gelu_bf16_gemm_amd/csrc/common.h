@@ -165,12 +165,10 @@ __device__ __forceinline__ Fp8RowFactor fp8_row_factor(float s) {
 // of h at most 9.1e-6 on [0, 6], absolute error of the GELU value at most 4.6e-7 for every v
 // (beyond |v| = 6, |v| h(6) < 1e-8 stands for |v| h(|v|)) — far below half a bf16 / fp16 /
 // E4M3 ulp of any output it produces. 10 VALU operations and one v_exp_f32 per element.
-__device__ __forceinline__ float gelu_erf_f32(float v) {
+__device__ __forceinline__ float gelu_erf_h(float x) {  // h for x = min(|v|, 6)
   constexpr float C0 = -9.999869466e-01f, C1 = -1.151324630e+00f, C2 = -4.582974911e-01f,
                   C3 = -5.411827192e-02f, C4 = 8.582354523e-03f, C5 = -9.488665964e-04f,
                   C6 = 6.386001041e-05f, C7 = -1.944896667e-06f;
-  const float a = fabsf(v);
-  const float x = fminf(a, 6.0f);
   float p = __builtin_fmaf(C7, x, C6);
   p = __builtin_fmaf(p, x, C5);
   p = __builtin_fmaf(p, x, C4);
@@ -178,8 +176,21 @@ __device__ __forceinline__ float gelu_erf_f32(float v) {
   p = __builtin_fmaf(p, x, C2);
   p = __builtin_fmaf(p, x, C1);
   p = __builtin_fmaf(p, x, C0);
-  const float h = __builtin_amdgcn_exp2f(p);
-  return __builtin_fmaf(-a, h, fmaxf(v, 0.f));
+  return __builtin_amdgcn_exp2f(p);
+}
+__device__ __forceinline__ float gelu_erf_f32(float v) {
+  const float a = fabsf(v);
+  return __builtin_fmaf(-a, gelu_erf_h(fminf(a, 6.0f)), fmaxf(v, 0.f));
+}
+// The same for v read straight from an accumulator register: float min / max would first quiet
+// such an operand (one more instruction per use, since the compiler cannot tell it is not a
+// signalling NaN), so |v|, min(|v|, 6) and max(v, 0) are taken as integer operations on the bit
+// pattern (non-negative floats order as their bit patterns). For v produced by arithmetic the
+// float form above is shorter.
+__device__ __forceinline__ float gelu_erf_acc_f32(float v) {
+  const uint32_t ub = __float_as_uint(v) & 0x7fffffffu;
+  const float x = __uint_as_float(min(ub, 0x40c00000u));  // 0x40c00000 = 6.0f
+  return __builtin_fmaf(-__uint_as_float(ub), gelu_erf_h(x), __int_as_float(max(__float_as_int(v), 0)));
 }
 
 // GELU, erf form, for fp32 outputs: the same v Phi(v) = max(v, 0) - |v| h with h = 0.5 erfc(|v| / sqrt 2)
