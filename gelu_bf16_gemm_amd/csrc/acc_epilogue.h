@@ -236,11 +236,12 @@ __device__ __forceinline__ void z_pass_to_lds(const EpiParams& e, const Cfg& cfg
   lds_barrier();
 }
 
-// Whether a configuration's accumulators start from the residual (see seed_residual), or,
-// with no residual, from the bias (written by the LDS-DMA mainloop before its first MFMA).
+// Whether a configuration's accumulators start from the residual (see seed_residual; a 16-bit
+// residual, whose 256 x 256 tile fits the 128 KB of LDS at once), or, with no residual, from the
+// bias (written by the LDS-DMA mainloop before its first MFMA).
 template <uint32_t F>
 constexpr bool seeds_residual() {
-  return (F & epi::kStatic) != 0 && (F & epi::kZ) != 0;
+  return (F & epi::kStatic) != 0 && (F & epi::kZ) != 0 && ((F >> epi::kZShift) & 3) != FUSEDOPS_F32;
 }
 // (Not with RoPE: that instance measured 660 B of spills per lane seeded against 56 unseeded.)
 template <uint32_t F>
@@ -265,35 +266,28 @@ __device__ __forceinline__ void seed_residual(const GemmArgs& a, f32x16 (&acc)[4
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wf = wave >> 1, wt = wave & 1;
   const int hb = lane >> 5, tl = lane & 31;
+  static_assert(seeds_residual<F>(), "a 16-bit residual: the whole tile in one pass");
   const int zdt = cfg.z_dt();
-  const int es = dt_bytes(zdt);
-  const int C = kTileCols * es / 16;
-  constexpr int passes = (kTileRows * kTileCols * (((F >> epi::kZShift) & 3) == FUSEDOPS_F32 ? 4 : 2)) > kStageBytes ? 2 : 1;
-  constexpr int R = kTileRows / passes;
+  constexpr int es = 2;
+  constexpr int C = kTileCols * es / 16;
+  z_pass_to_lds(e, cfg, lds, t0, f0, a.M, a.N, 0, kTileRows, C);
 #pragma unroll
-  for (int p = 0; p < passes; ++p) {
-    if (p > 0) lds_barrier();  // every wave has read the previous pass
-    z_pass_to_lds(e, cfg, lds, t0, f0, a.M, a.N, p, R, C);
-    if (passes == 1 || wt == p) {
+  for (int fb = 0; fb < 4; ++fb) {
+    f32x4 b[4] = {};
+    if (cfg.bias()) {
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb) {
-        f32x4 b[4] = {};
-        if (cfg.bias()) {
+      for (int q = 0; q < 4; ++q) b[q] = *reinterpret_cast<const f32x4*>(svec + wf * 128 + fb * 32 + q * 8 + hb * 4);
+    }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) b[q] = *reinterpret_cast<const f32x4*>(svec + wf * 128 + fb * 32 + q * 8 + hb * 4);
-        }
+    for (int tb = 0; tb < 4; ++tb) {
+      const int r = wt * 128 + tb * 32 + tl;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const int r = wt * 128 + tb * 32 + tl - p * R;
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 z = lds_get4(lds, st_off(r, (wf * 128 + fb * 32 + q * 8 + hb * 4) * es, C), zdt);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 z = lds_get4(lds, st_off(r, (wf * 128 + fb * 32 + q * 8 + hb * 4) * es, C), zdt);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[fb][tb][4 * q + j] = z[j] + b[q][j];
-          }
-          to_agpr<F>(acc[fb][tb]);
-        }
+        for (int j = 0; j < 4; ++j) acc[fb][tb][4 * q + j] = z[j] + b[q][j];
       }
+      to_agpr<F>(acc[fb][tb]);
     }
   }
   lds_barrier();  // every wave has read its groups: `lds` is free

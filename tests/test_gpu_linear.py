@@ -333,6 +333,10 @@ def test_dma_mainloop_epilogue_instances():
     run_linear(300, 512, 256, bias=True, act="gelu_tanh", out_dtype=I.F32, seed=4)      # generic instance
     run_linear(300, 768, 256, bias=True, split=3, rope=64, seed=5)                      # generic, RoPE
     run_linear(300, 512, 256, residual=True, gamma=True, inplace=True, pad=24, seed=6)  # in place, padded rows
+    # the out-projection instance starts its accumulators from the residual rows: with the output
+    # written over the residual, and with padded rows
+    run_linear(300, 512, 256, residual=True, aux=True, partials=True, gamma=True, inplace=True, seed=7)
+    run_linear(300, 512, 256, residual=True, aux=True, partials=True, gamma=True, pad=8, seed=8)
 
 
 # ---------------------------------------------------------------------------
