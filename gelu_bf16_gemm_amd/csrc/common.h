@@ -162,9 +162,11 @@ __device__ __forceinline__ Fp8RowFactor fp8_row_factor(float s) {
 // itself (no cancellation in the negative tail). h is computed with one transcendental as
 // 2^p(a), where p is a degree-7 polynomial in a = min(|v|, 6) fitted to log2 h (Chebyshev least
 // squares on [0, 6], coefficients rounded to fp32, evaluated by Horner in fp32): relative error
-// of h at most 9.1e-6 on [0, 6], absolute error of the GELU value at most 4.6e-7 for every v
-// (beyond |v| = 6, |v| h(6) < 1e-8 stands for |v| h(|v|)) — far below half a bf16 / fp16 /
-// E4M3 ulp of any output it produces. 10 VALU operations and one v_exp_f32 per element.
+// of h at most 9.1e-6 on [0, 6], absolute error of the GELU value at most 4.6e-7 for |v| <= 6.
+// Beyond, |v| h(6) (h(6) = 9.9e-10) stands for |v| h(|v|): the result is off by at most 9.9e-10 |v|,
+// a relative 1e-9 of v for v > 6 and, for v < -6, a value below 1e-9 |v| where the exact one is
+// below 1e-9 too. All of it is far below half a bf16 / fp16 / E4M3 ulp of the output's scale.
+// 10 VALU operations and one v_exp_f32 per element.
 __device__ __forceinline__ float gelu_erf_h(float x) {  // h for x = min(|v|, 6)
   constexpr float C0 = -9.999869466e-01f, C1 = -1.151324630e+00f, C2 = -4.582974911e-01f,
                   C3 = -5.411827192e-02f, C4 = 8.582354523e-03f, C5 = -9.488665964e-04f,
