@@ -43,7 +43,7 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "fused GEMM+epilogue TFLOP/s (%MFMA peak); LN+GELU GB/s (%HBM peak)"
 
-# (workload, bound) in step order; "hbm" workloads are judged on GB/s
+# (workload, bound) in step order; "hbm" workloads are rated in GB/s against the HBM peak
 SUITE = [
     ("ln_gelu_f16_32768x4096", "hbm"),
     ("ln_gelu_f16_32768x3000", "hbm"),
@@ -302,7 +302,7 @@ def main() -> int:
                          "so that HBM byte counters can be scaled against a known size")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the row-split sharding needs no exchange and is described in the design notes)",
               file=sys.stderr)
         return 2

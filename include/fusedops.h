@@ -50,7 +50,7 @@ extern "C" {
 enum fusedops_status {
   FUSEDOPS_OK = 0,
   FUSEDOPS_ERR_INVALID_ARG = -1,  /* null required pointer, bad size, bad enum, bad op list, aliasing */
-  FUSEDOPS_ERR_UNSUPPORTED = -2,  /* valid request that this build has no kernel for */
+  FUSEDOPS_ERR_UNSUPPORTED = -2,  /* valid request that the library has no kernel for */
   FUSEDOPS_ERR_MISALIGNED = -3,   /* pointer / leading dimension / width alignment rule broken */
   FUSEDOPS_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required */
   FUSEDOPS_ERR_LAUNCH = -5        /* the HIP runtime refused this call's kernel launch */
