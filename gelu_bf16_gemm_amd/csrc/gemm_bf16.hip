@@ -475,7 +475,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   __shared__ __attribute__((aligned(16))) float svec[4 * 256];               // epilogue vectors
   __shared__ int slot[2];
 
-  if (a.ep.quant) {
+  // A static configuration fixes quant() at compile time: the instances without FP8 rows carry
+  // no code for them (which also leaves the compiler fewer values to keep across the walk).
+  const epi::Cfg<F> cfg{a.ep};
+  if (cfg.quant()) {
     int tt, ft;
     if (a.ep.tickets) {
       // FP8 row scales need every feature tile of a token block: hand out tiles in
