@@ -317,6 +317,13 @@ def test_dma_mainloop_bias_gelu_erf(M, N, K):
     run_linear(M, N, K, bias=True, act="gelu_erf")
 
 
+# the residual op list on the same shapes: its accumulators start from the residual rows, and
+# the last token tile's rows past M read as zero there
+@pytest.mark.parametrize("M,N,K", [(129, 256, 128), (257, 256, 128), (300, 512, 384), (520, 768, 1024)])
+def test_dma_mainloop_residual_seed(M, N, K):
+    run_linear(M, N, K, residual=True, aux=True, partials=True, gamma=True, seed=3)
+
+
 # more tiles than CUs: resident workgroups walk several tiles each (LDS-DMA and register-staged
 # mainloops, ragged last token tile, ragged N in the second)
 @pytest.mark.parametrize("M,N,K", [(2300, 8192, 128), (2300, 8200, 136)])
