@@ -19,7 +19,9 @@
 //     token-major, XOR-swizzled LDS tile, and the workgroup then stores whole rows with
 //     16-byte coalesced writes (plain, or split across up to three destinations).
 // Residual rows come in the other direction: a coalesced copy into the same LDS tile
-// layout, then per-group reads.
+// layout, then per-group reads. On the LDS-DMA path the static configurations with a bias or
+// a 16-bit residual do that before the mainloop instead and start the accumulators from those
+// values (seed_residual, or the bias in the mainloop's prologue), so the epilogue adds neither.
 #pragma once
 
 #include "epilogue.h"
