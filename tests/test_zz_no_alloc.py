@@ -57,7 +57,8 @@ def quant_pair(M, N, K, seed):
 
 
 @pytest.mark.parametrize("first,second", [((64, 4096, 512), (17, 1024, 256)),     # few-token kernel
-                                          ((600, 2048, 256), (300, 1056, 136))])  # 256 x 256 tiles
+                                          ((600, 2048, 256), (300, 1056, 136)),   # 256 x 256 tiles
+                                          ((2300, 8192, 128), (600, 2048, 256))])  # more tiles than resident: tickets
 def test_noalloc_matches_regular_entry_point(first, second):
     for shape in (first, second):
         (qa, sa), (qb, sb) = quant_pair(*shape, seed=1)
