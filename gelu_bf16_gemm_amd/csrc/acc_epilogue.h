@@ -370,10 +370,13 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     if (cfg.gamma()) v *= g;
     if (cfg.rscale()) v *= rs_of(tb);
     if (act == ACT_GELU_ERF) {
-      // a seeded tile with no scale feeds the accumulators straight in
+      // a seeded tile with no scale feeds the accumulators straight in; a static bf16 output
+      // takes the degree-6 h
       constexpr bool raw = kSeeded && (F & (epi::kGamma | epi::kRscale)) == 0;
+      constexpr bool bf16 = (F & epi::kStatic) != 0 && ((F >> epi::kYShift) & 3) == FUSEDOPS_BF16 &&
+                            (F & epi::kQuant) == 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = raw ? gelu_erf_acc_f32(v[r]) : gelu_erf_f32(v[r]);
+      for (int r = 0; r < 16; ++r) v[r] = raw ? gelu_erf_acc_f32<bf16>(v[r]) : gelu_erf_f32<bf16>(v[r]);
     } else if (act == ACT_GELU_TANH) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) v[r] = gelu_tanh_f32(v[r]);

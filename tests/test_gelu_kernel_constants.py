@@ -20,30 +20,35 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
                    "common.h")
 
 
-def _coefficients():
+# the kernels' two forms of h: degree 7 for any 16-bit or E4M3 output, degree 6 for bf16 outputs
+FORMS = {"gelu_erf_h": 8, "gelu_erf_h_bf16": 7}  # function -> number of coefficients
+
+
+def _coefficients(name="gelu_erf_h"):
     text = open(SRC).read()
-    body = text[text.index("float gelu_erf_h(float x)"):]
+    body = text[text.index(f"float {name}(float x)"):]
     body = body[:body.index("}")]
     found = dict(re.findall(r"\b(C\d)\s*=\s*([-+0-9.eE]+)f", body))
-    assert sorted(found) == [f"C{i}" for i in range(8)], found
-    return [np.float32(float(found[f"C{i}"])) for i in range(8)]
+    n = FORMS[name]
+    assert sorted(found) == [f"C{i}" for i in range(n)], found
+    return [np.float32(float(found[f"C{i}"])) for i in range(n)]
 
 
-def _h_kernel(x32):
+def _h_kernel(x32, name="gelu_erf_h"):
     """2^p(x) with p evaluated as the kernel does: fp32, one rounding per fused multiply-add."""
-    c = _coefficients()
-    p = np.full_like(x32, c[7])
-    for k in range(6, -1, -1):
+    c = _coefficients(name)
+    p = np.full_like(x32, c[-1])
+    for k in range(len(c) - 2, -1, -1):
         # fma(p, x, c_k) rounded once: exact in fp64 for fp32 operands, then rounded to fp32
         p = (p.astype(np.float64) * x32.astype(np.float64) + np.float64(c[k])).astype(np.float32)
     return np.exp2(p.astype(np.float64))  # the hardware exp2 is within an ulp; exact here
 
 
-def _gelu_kernel(v):
+def _gelu_kernel(v, name="gelu_erf_h"):
     v = np.asarray(v, np.float64)
     a = np.abs(v).astype(np.float32)
     x = np.minimum(a, np.float32(6.0))
-    return np.maximum(v, 0.0) - a.astype(np.float64) * _h_kernel(x)
+    return np.maximum(v, 0.0) - a.astype(np.float64) * _h_kernel(x, name)
 
 
 def test_h_relative_error_on_the_fitted_range():
@@ -73,3 +78,18 @@ def test_gelu_special_values():
     # Phi(1) = 0.841344746..., so GELU(1) = 0.841344746 and GELU(-1) = -0.158655254
     assert abs(_gelu_kernel(1.0) - 0.8413447460685429) < 1e-6
     assert abs(_gelu_kernel(-1.0) + 0.15865525393145707) < 1e-6
+
+
+def test_bf16_form_bounds():
+    # degree 6 for bf16 outputs: h within 4.9e-5, the GELU value within 6.6e-6 for |v| <= 6 and
+    # within 9.9e-10 |v| beyond (h(6) clamped), all far below half a bf16 ulp (2^-9 of the value)
+    x = np.linspace(0.0, 6.0, 600001).astype(np.float32)
+    h = 0.5 * erfc(x.astype(np.float64) / np.sqrt(2.0))
+    rel = np.abs(_h_kernel(x, "gelu_erf_h_bf16") / h - 1.0)
+    assert rel.max() <= 4.9e-5, rel.max()
+    v = np.linspace(-6.0, 6.0, 600001)
+    err = np.abs(_gelu_kernel(v, "gelu_erf_h_bf16") - v * 0.5 * erfc(-v / np.sqrt(2.0)))
+    assert err.max() <= 6.6e-6, err.max()
+    v = np.concatenate([np.linspace(-40.0, -6.0, 100001), np.linspace(6.0, 40.0, 100001)])
+    err = np.abs(_gelu_kernel(v, "gelu_erf_h_bf16") - v * 0.5 * erfc(-v / np.sqrt(2.0)))
+    assert (err <= 9.9e-10 * np.abs(v)).all()
