@@ -130,7 +130,7 @@ struct Dest {
 // nontemporal: an output tile is written once, and kept in L2 its dirty lines would be
 // written back later while the next tiles' operand loads need the space (measured on the
 // out-projection, whose h1 and h2 are 2 M N bf16 per launch: 167.8 -> 143.1 us).
-__device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int row0, int M, const Dest& d) {
+__device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int row0, int M, const Dest& d, int tid) {
   const int cshift = __builtin_ctz(C);
   const int per = 16 / d.es;  // elements per chunk
   const int sw = (int)d.split_w;
@@ -141,10 +141,10 @@ __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int r
   const int col_end = d.col0 + C * per;
   const int seg0 = sw ? d.col0 / sw : 0;
   if (row0 + R <= M && col_end <= d.cols && (!sw || (col_end - 1) / sw == seg0)) {
-    const int c = threadIdx.x & (C - 1);
+    const int c = tid & (C - 1);
     const int rstep = kEpiThreads >> cshift;
     const int m = (C < 32 ? C : 32) - 1;
-    int r = threadIdx.x >> cshift;
+    int r = tid >> cshift;
     uint8_t* g = d.at(seg0) + ((int64_t)(row0 + r) * d.ld + (d.col0 - seg0 * sw) + c * per) * d.es;
     const int64_t gstep = (int64_t)rstep * d.ld * d.es;
 #pragma unroll 8
@@ -154,7 +154,7 @@ __device__ __forceinline__ void copy_out(const uint8_t* lds, int R, int C, int r
     return;
   }
 #pragma unroll 8
-  for (int id = threadIdx.x; id < R * C; id += kEpiThreads) {
+  for (int id = tid; id < R * C; id += kEpiThreads) {
     const int r = id >> cshift, c = id & (C - 1);
     const int t = row0 + r;
     const int col = d.col0 + c * per;
@@ -302,14 +302,17 @@ __device__ __forceinline__ void seed_residual(const GemmArgs& a, f32x16 (&acc)[4
 // `svec` the tile's vectors (VecPrefetch); every thread of the workgroup must call this.
 // kSeeded: the accumulators started from the residual and the bias (seed_residual, or the bias
 // alone when there is no residual), so neither is added here.
+// tid: the thread index. A caller may pass an opaque copy, so that the per-lane constants are
+// recomputed in every tile of a walk instead of computed once and, short of registers, spilled:
+// a reload waits for every load in flight, including DMAs issued for the next tile.
 template <uint32_t F, bool kSeeded = false>
 __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, const float* svec,
-                                             int t0, int f0, int ft, int* slot) {
+                                             int t0, int f0, int ft, int* slot, int tid) {
   using namespace accepi;
   const EpiParams& e = a.ep;
   const epi::Cfg<F> cfg{e};
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave >> 1, wt = wave & 1;
   const int hb = lane >> 5, tl = lane & 31;
   const int M = a.M, N = a.N;
@@ -349,7 +352,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
           }
       }
       lds_barrier();
-      copy_out(lds, R, C, t0 + p * R, M, d);
+      copy_out(lds, R, C, t0 + p * R, M, d, tid);
     }
   };
 

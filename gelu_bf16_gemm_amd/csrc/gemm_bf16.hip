@@ -38,6 +38,7 @@ constexpr int BT = 256;   // tokens per tile
 constexpr int BK = 64;    // K per step
 constexpr int kThreads = 256;
 constexpr int kTileBytes = 256 * BK * 2;  // one operand tile in LDS (32 KB)
+constexpr int kBuf = 2 * kTileBytes;      // one stage: W tile then X tile
 
 // One 16-byte-per-lane LDS DMA: lane l's 16 bytes at rsrc + soff + voff land at LDS byte
 // lds + 16 l. Issued as inline assembly so that the compiler, which cannot tell the DMA's LDS
@@ -56,6 +57,87 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 template <int N>
 __device__ __forceinline__ void dma_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// The per-lane addressing of one tile's operand DMAs on the LDS-DMA path. One DMA instruction
+// fills 8 consecutive LDS rows (1 KB): lane l writes position l % 8 of row l / 8, which holds
+// logical chunk (l % 8) ^ swz(row). For a group of rows starting at a multiple of 8, swz(row) =
+// l / 8 ^ (bit 3 of the group's first row). Step t goes to stage t & 1; DMAs of steps past the
+// last read nothing (the offset's top bit puts them out of range) and leave LDS as it is.
+struct DmaPlan {
+  const GemmArgs& a;
+  __amdgpu_buffer_rsrc_t rW, rX;
+  uint32_t lds0;          // LDS byte address of the stages
+  int wave;
+  uint32_t w_lane[2];     // W row group g of a block
+  uint32_t x_lane[2][4];  // X token half h, row group g (rows past M read row M - 1)
+
+  // tid: the thread index (the caller may pass an opaque copy, see mainloop_dma)
+  __device__ __forceinline__ DmaPlan(const GemmArgs& args, uint8_t* smem, int t0, int f0, int tid) : a(args) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int x_rows = min(BT, a.M - t0);
+    const uint16_t* Wt = static_cast<const uint16_t*>(a.W) + (int64_t)f0 * a.ldw;
+    const uint16_t* Xt = static_cast<const uint16_t*>(a.X) + (int64_t)t0 * a.ldx;
+    rW = make_rsrc(Wt, (uint32_t)(((int64_t)(BF - 1) * a.ldw + a.K) * 2));
+    rX = make_rsrc(Xt, (uint32_t)(((int64_t)(x_rows - 1) * a.ldx + a.K) * 2));
+    lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
+    const int l8 = lane >> 3, p8 = lane & 7;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) w_lane[g] = (uint32_t)(l8 * a.ldw * 2 + ((p8 ^ l8 ^ g) << 4));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r = min(x_row0(h) + g * 8 + l8, x_rows - 1);
+        x_lane[h][g] = (uint32_t)(r * a.ldx * 2 + ((p8 ^ l8 ^ (g & 1)) << 4));
+      }
+  }
+  // W: wave w fills rows (w >> 1) * 128 + j * 32 + (w & 1) * 16 + g * 8 .. of block j, g = 0, 1
+  __device__ __forceinline__ int w_row0() const { return (wave >> 1) * 128 + (wave & 1) * 16; }
+  // X: token half h of the tile is token blocks 2h and 2h + 1 of both 128-token halves (what
+  // every wave reads for those blocks); wave w fills its rows x_row0(h) + g * 8 .., g = 0..3
+  __device__ __forceinline__ int x_row0(int h) const { return (wave >> 1) * 128 + (2 * h + (wave & 1)) * 32; }
+  __device__ __forceinline__ int steps() const { return a.K / BK; }
+  __device__ __forceinline__ void w1(int t, int j, int g) const {
+    const uint32_t oob = t < steps() ? 0u : kOobOffset;
+    const int r0 = w_row0() + j * 32 + g * 8;
+    lds_dma16(rW, w_lane[g] | oob, (uint32_t)(r0 * a.ldw * 2 + t * BK * 2), lds0 + (t & 1) * kBuf + r0 * 128);
+  }
+  __device__ __forceinline__ void x1(int t, int h, int g) const {
+    const uint32_t oob = t < steps() ? 0u : kOobOffset;
+    lds_dma16(rX, x_lane[h][g] | oob, (uint32_t)(t * BK * 2), lds0 + (t & 1) * kBuf + kTileBytes + (x_row0(h) + g * 8) * 128);
+  }
+  __device__ __forceinline__ void w(int t, int j) const { w1(t, j, 0); w1(t, j, 1); }
+  __device__ __forceinline__ void x(int t, int h) const {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) x1(t, h, g);
+  }
+  // A tile's first 16 DMAs per wave, in the prologue's order: all of step 0 (stage 0 only).
+  __device__ __forceinline__ void head() const { x(0, 0); x(0, 1); w(0, 0); w(0, 1); w(0, 2); w(0, 3); }
+};
+
+// Static configurations whose epilogue leaves LDS stage 0 alone: SwiGLU halves in 16 bits
+// (a 64 KB staged tile, placed in stage 1) and the cross-entropy statistics (nothing staged
+// unless the logits are stored, which is checked at run time). In the tile walk they issue the
+// next tile's first DMAs (DmaPlan::head) as soon as the mainloop is done, so that data lands
+// while the epilogue runs instead of at the start of the next tile.
+template <uint32_t F>
+constexpr bool prefetches_head() {
+  constexpr uint32_t kStages = epi::kZ | epi::kAux | epi::kPart | epi::kQuant | epi::kSplit | epi::kRope;
+  if ((F & epi::kStatic) == 0 || (F & kStages) != 0) return false;
+  if ((F & epi::kXent) != 0) return true;
+  constexpr int y = (F >> epi::kYShift) & 3;
+  return ((F >> epi::kActShift) & 3) == ACT_SWIGLU && (y == FUSEDOPS_BF16 || y == FUSEDOPS_F16);
+}
+
+// Of those, the ones without a bias (which would start the accumulators in the mainloop):
+// only their epilogue reads the per-feature / per-token vectors, which are then stored to LDS
+// after the mainloop. Stored in the prologue, they would need the wait for their loads there,
+// which the compiler places after the prologue's DMAs, draining them.
+template <uint32_t F>
+constexpr bool late_vectors() {
+  return prefetches_head<F>() && (F & epi::kBias) == 0;
 }
 
 // Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
@@ -93,8 +175,8 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 // first barrier has made the LDS copy of the vectors visible) instead of from zero.
 template <uint32_t F, bool kBiasStart>
 __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, float* svec,
-                                             const accepi::VecPrefetch& vp, f32x16 (&acc)[4][4], int t0, int f0) {
-  constexpr int kBuf = 2 * kTileBytes;  // one stage: W tile then X tile
+                                             const accepi::VecPrefetch& vp, f32x16 (&acc)[4][4], int t0, int f0,
+                                             bool head_loaded) {
   // The per-lane DMA and fragment offsets below are the same for every tile, so the compiler
   // would compute them once, keep them live across the whole tile walk and, short of registers,
   // spill them; each reload in the prologue then needs vmcnt(0), which also waits for every DMA
@@ -102,55 +184,19 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   // recomputed (a few dozen VALU ops per tile) instead.
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const DmaPlan d(a, smem, t0, f0, tid);
+  const int wave = d.wave, lane = tid & 63;
   const int wf = wave >> 1, wt = wave & 1;
-  const int K = a.K;
-  const int steps = K / BK;
-  const int x_rows = min(BT, a.M - t0);
-  const uint16_t* Wt = static_cast<const uint16_t*>(a.W) + (int64_t)f0 * a.ldw;
-  const uint16_t* Xt = static_cast<const uint16_t*>(a.X) + (int64_t)t0 * a.ldx;
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wt, (uint32_t)(((int64_t)(BF - 1) * a.ldw + K) * 2));
-  const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xt, (uint32_t)(((int64_t)(x_rows - 1) * a.ldx + K) * 2));
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;  // LDS byte address of smem
-
-  // One DMA instruction fills 8 consecutive LDS rows (1 KB): lane l writes position l % 8 of
-  // row l / 8, which holds logical chunk (l % 8) ^ swz(row). For a group of rows starting at a
-  // multiple of 8, swz(row) = l / 8 ^ (bit 3 of the group's first row).
-  const int l8 = lane >> 3, p8 = lane & 7;
-  // W: wave w fills rows (w >> 1) * 128 + j * 32 + (w & 1) * 16 + g * 8 .. of block j, g = 0, 1
-  const int w_row0 = (wave >> 1) * 128 + (wave & 1) * 16;
-  uint32_t w_lane[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) w_lane[g] = (uint32_t)(l8 * a.ldw * 2 + ((p8 ^ l8 ^ g) << 4));
-  // X: token half h of the tile is token blocks 2h and 2h + 1 of both 128-token halves (what
-  // every wave reads for those blocks); wave w fills its rows x_row0(h) + g * 8 .., g = 0..3
-  // (rows past M read row M - 1)
-  auto x_row0 = [&](int h) __attribute__((always_inline)) { return (wave >> 1) * 128 + (2 * h + (wave & 1)) * 32; };
-  uint32_t x_lane[2][4];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int r = min(x_row0(h) + g * 8 + l8, x_rows - 1);
-      x_lane[h][g] = (uint32_t)(r * a.ldx * 2 + ((p8 ^ l8 ^ (g & 1)) << 4));
-    }
-  // DMAs of steps past the last read nothing (the offset's top bit puts them out of range)
-  // and leave LDS as it is; they are still issued so that the wait counts stay exact.
-  auto dma_w1 = [&](int t, int j, int g) __attribute__((always_inline)) {
-    const uint32_t oob = t < steps ? 0u : kOobOffset;
-    const int r0 = w_row0 + j * 32 + g * 8;
-    lds_dma16(rW, w_lane[g] | oob, (uint32_t)(r0 * a.ldw * 2 + t * BK * 2), lds0 + (t & 1) * kBuf + r0 * 128);
-  };
-  auto dma_x1 = [&](int t, int h, int g) __attribute__((always_inline)) {
-    const uint32_t oob = t < steps ? 0u : kOobOffset;
-    lds_dma16(rX, x_lane[h][g] | oob, (uint32_t)(t * BK * 2),
-              lds0 + (t & 1) * kBuf + kTileBytes + (x_row0(h) + g * 8) * 128);
-  };
-  auto dma_w = [&](int t, int j) __attribute__((always_inline)) { dma_w1(t, j, 0); dma_w1(t, j, 1); };
-  auto dma_x = [&](int t, int h) __attribute__((always_inline)) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) dma_x1(t, h, g);
-  };
+  // With the next tile's head prefetched, the step count is opaque too: the loop's entry test
+  // would otherwise be hoisted out of the walk and held across every tile, and spilled, its
+  // reload waiting for the DMAs in flight. (The other instances measured more spills with it.)
+  int steps = a.K / BK;
+  if constexpr (prefetches_head<F>()) asm volatile("" : "+s"(steps));
+  // DMAs of steps past the last are still issued so that the wait counts stay exact.
+  auto dma_w1 = [&](int t, int j, int g) __attribute__((always_inline)) { d.w1(t, j, g); };
+  auto dma_x1 = [&](int t, int h, int g) __attribute__((always_inline)) { d.x1(t, h, g); };
+  auto dma_w = [&](int t, int j) __attribute__((always_inline)) { d.w(t, j); };
+  auto dma_x = [&](int t, int h) __attribute__((always_inline)) { d.x(t, h); };
 
   // Operand fragments: row (lane % 32) of a 32-row block, logical chunk 2 kk + lane / 32.
   const int a_row0 = wf * 128 + (lane & 31);
@@ -222,13 +268,21 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   // Prologue: X and W blocks 0-1 of step 0, then the loop's own DMA order from region B of
   // step -2 (W blocks 2-3 of step 0, X half 0 of step 1) and region A of step -1 (W blocks
   // 0-1 and X half 1 of step 1); the fragments of step 0; region B of step -1 (W blocks 2-3 of
-  // step 1, X half 0 of step 2, into space the step-0 fragments were read from).
-  dma_x(0, 0); dma_x(0, 1);
-  dma_w(0, 0); dma_w(0, 1);
-  dma_w(0, 2); dma_w(0, 3); dma_x(1, 0);
+  // step 1, X half 0 of step 2, into space the step-0 fragments were read from). With
+  // head_loaded the previous tile's epilogue issued all of step 0 (DmaPlan::head) and the first
+  // wait takes it whole, with the stores issued after it; from the next wait on, the DMAs in
+  // flight are the same either way.
+  head_loaded = prefetches_head<F>() && head_loaded;
+  if (!head_loaded) {  // the same DMAs as DmaPlan::head
+    dma_x(0, 0); dma_x(0, 1);
+    dma_w(0, 0); dma_w(0, 1);
+    dma_w(0, 2); dma_w(0, 3);
+  }
+  dma_x(1, 0);
   dma_w(1, 0); dma_w(1, 1); dma_x(1, 1);
-  if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
-  dma_wait_barrier<16>();  // X and W blocks 0-1 of step 0
+  if constexpr ((F & epi::kStatic) != 0 && !late_vectors<F>()) vp.store(svec);
+  if (head_loaded) dma_wait_barrier<12>();  // step 0, and every store before this tile
+  else dma_wait_barrier<16>();              // X and W blocks 0-1 of step 0
   if constexpr (kBiasStart) {
     // register 4q + j of block (fb, tb) holds feature wf*128 + fb*32 + 8q + 4*(lane/32) + j
 #pragma unroll
@@ -266,18 +320,24 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   dma_wait_barrier<0>();  // every DMA has landed and every fragment read is done before LDS is reused
 }
 
-// One output tile (token tile tt, feature tile ft): mainloop and epilogue.
+// One output tile (token tile tt, feature tile ft): mainloop and epilogue. head_loaded: the
+// previous tile issued this tile's head DMAs. next_tt >= 0 names the workgroup's next tile;
+// returns whether this tile issued that tile's head DMAs.
 template <uint32_t F, bool kDma>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uint8_t* smem, float* svec, int* slot) {
+__device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int tt, int ft, uint8_t* smem, float* svec, int* slot,
+                                          bool head_loaded = false, int next_tt = -1, int next_ft = 0) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wf = wave >> 1, wt = wave & 1;
   const int f0 = ft * BF, t0 = tt * BT;
   const int K = a.K;
 
-  // the epilogue's per-feature / per-token vectors, fetched now and kept in LDS
+  // the epilogue's per-feature / per-token vectors, fetched now and kept in LDS (a row scale
+  // that late_vectors stores after the mainloop is also fetched there: it is computed from
+  // its loads at once, and the waits for them would delay the prologue's DMAs)
+  constexpr bool kLateLoad = kDma && late_vectors<F>() && (F & epi::kRscale) != 0;
   accepi::VecPrefetch vp;
-  if constexpr ((F & epi::kStatic) != 0) vp.load<F>(a.ep, t0, f0, a.M, a.N);
+  if constexpr ((F & epi::kStatic) != 0 && !kLateLoad) vp.load<F>(a.ep, t0, f0, a.M, a.N);
 
   // On the LDS-DMA path a static configuration's accumulators start from its residual and
   // bias (seed_residual) or, without a residual, from its bias (in mainloop_dma): the MFMAs
@@ -297,8 +357,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uin
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   }
 
+  bool next_head = false;
+  int tid_e = tid;  // the epilogue's thread index
   if constexpr (kDma) {
-    mainloop_dma<F, kSeed && !accepi::seeds_residual<F>()>(a, smem, svec, vp, acc, t0, f0);
+    mainloop_dma<F, kSeed && !accepi::seeds_residual<F>()>(a, smem, svec, vp, acc, t0, f0, head_loaded);
+    if constexpr (late_vectors<F>()) {
+      if constexpr (kLateLoad) vp.load<F>(a.ep, t0, f0, a.M, a.N);
+      vp.store(svec);  // nothing is in flight here
+      lds_barrier();
+    }
+    if constexpr (prefetches_head<F>()) {
+      // An opaque copy of the thread index, taken before the DMAs: the epilogue's lane
+      // constants then come from it, and the thread index itself (held in scratch across the
+      // walk) is reloaded here, where nothing is in flight, not after the DMAs.
+      asm volatile("" : "+v"(tid_e));
+      // the mainloop's last barrier has retired every read of both stages
+      if (next_tt >= 0 && ((F & epi::kXent) == 0 || a.ep.y == nullptr)) {
+        DmaPlan(a, smem, next_tt * BT, next_ft * BF, tid_e).head();
+        next_head = true;
+      }
+    }
   } else {
     // Buffer resources over this tile's rows: rows past M / N read as zero.
     const int w_rows = min(BF, a.N - f0), x_rows = min(BT, a.M - t0);
@@ -450,8 +528,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uin
 
   if constexpr ((F & epi::kStatic) != 0) {
     // Epilogue on the accumulators in place; the mainloop's LDS buffers (128 KB) stage
-    // the finished values for coalesced stores.
-    acc_epilogue<F, kSeed>(a, acc, smem, svec, t0, f0, ft, slot);
+    // the finished values for coalesced stores (stage 1 alone when the next head may be in stage 0).
+    // (The stage-1 offset is passed opaque: as a constant it would be folded into every LDS
+    // access and overflow their 16-bit offset fields, costing an address add per access.)
+    uint8_t* lds = smem;
+    if constexpr (kDma && prefetches_head<F>() && (F & epi::kXent) == 0) {
+      int off = kBuf;
+      asm volatile("" : "+s"(off));
+      lds += off;
+    }
+    acc_epilogue<F, kSeed>(a, acc, lds, svec, t0, f0, ft, slot, tid_e);
   } else {
     // Any other op list: the fp32 tile is staged through LDS in two 128-token passes
     // (128 KB each; pass p takes the accumulators of the waves with wt == p) and the
@@ -467,6 +553,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tt, int ft, uin
             for (int tb = 0; tb < 4; ++tb) stage_block<BF>(tile, acc[fb][tb], wf * 128 + fb * 32, tb * 32);
         });
   }
+  return next_head;
 }
 
 template <uint32_t F, bool kDma>
@@ -497,13 +584,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_t256_kernel(GemmArgs a)
   // XCD each time, in the XCD-aware order), so a tile's first loads are issued while the
   // previous tile's stores are still in flight, and no workgroup launch sits between tiles.
   const int tiles = a.tiles_t * a.tiles_f;
+  bool head = false;  // this tile's head DMAs were issued by the previous one
 #pragma clang loop unroll(disable)
   for (int id = blockIdx.x; id < tiles; id += gridDim.x) {
     // the previous tile's epilogue is done with LDS (its global stores may still be in flight)
     if (id != (int)blockIdx.x) lds_barrier();
-    int tt, ft;
+    int tt, ft, ntt = -1, nft = 0;
     tile_coords(id, a.tiles_t, a.tiles_f, tt, ft);
-    gemm_tile<F, kDma>(a, tt, ft, smem, svec, slot);
+    if constexpr (kDma && prefetches_head<F>())
+      if (id + (int)gridDim.x < tiles) tile_coords(id + gridDim.x, a.tiles_t, a.tiles_f, ntt, nft);
+    const bool issued = gemm_tile<F, kDma>(a, tt, ft, smem, svec, slot, head, ntt, nft);
+    if constexpr (kDma && prefetches_head<F>()) head = issued;
   }
 }
 

@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_t256_kernel(GemmArgs a) 
   }
 
   if constexpr ((F & epi::kStatic) != 0) {
-    acc_epilogue<F>(a, acc, smem, svec, t0, f0, ft, slot);
+    acc_epilogue<F>(a, acc, smem, svec, t0, f0, ft, slot, threadIdx.x);
   } else {
     __shared__ float s_amax[BT];
     run_staged_epilogue<BF, 1, 128, 2>(

@@ -330,6 +330,10 @@ def test_dma_mainloop_residual_seed(M, N, K):
 def test_tile_walking_workgroups(M, N, K):
     run_linear(M, N, K, bias=True, act="gelu_erf", seed=11)
     run_linear(M, N, K, residual=True, aux=True, partials=True, gamma=True, seed=12)
+    # SwiGLU instances: with whole K steps each tile issues the next tile's first K step while
+    # its own epilogue runs (the last token tile ragged, so that tile's rows differ)
+    run_linear(M, N, K, act="swiglu", seed=13)
+    run_linear(M, N, K, rscale=True, act="swiglu", seed=14)
 
 
 def test_dma_mainloop_epilogue_instances():
@@ -884,6 +888,14 @@ def run_xent(M, N, K, *, store_logits=False, bias=False, act=None, in_dtype=I.BF
                                    (300, 1001, 136), (257, 50257, 256)])
 def test_xent_statistics_and_loss(M, N, K):
     run_xent(M, N, K)
+
+
+# the LM-head instance over more tiles than CUs (3 x 128 tiles, the last token tile ragged):
+# without stored logits each tile issues the next tile's first K step during its epilogue, with
+# them it does not (the staged logits take all of LDS)
+def test_xent_tile_walking():
+    run_xent(600, 32768, 128)
+    run_xent(600, 32768, 128, store_logits=True, seed=1)
 
 
 def test_xent_with_logits_bias_activation_and_fp8_inputs():
