@@ -103,9 +103,9 @@ struct VecPrefetch {
     v[2] = cfg.rscale() && t < M ? row_scale_of(e, t) : 0.f;
     lab = cfg.xent() && t < M ? e.xent_labels[t] : -1;
   }
-  // svec: [0, 256) bias, [256, 512) column scale, [512, 768) row scale, [768, 1024) label bits
-  __device__ __forceinline__ void store(float* svec) const {
-    const int tid = threadIdx.x;
+  // svec: [0, 256) bias, [256, 512) column scale, [512, 768) row scale, [768, 1024) label bits.
+  // tid: the thread index (a caller may pass an opaque copy, as for acc_epilogue)
+  __device__ __forceinline__ void store(float* svec, int tid) const {
     svec[tid] = v[0];
     svec[256 + tid] = v[1];
     svec[512 + tid] = v[2];
@@ -305,7 +305,8 @@ __device__ __forceinline__ void seed_residual(const GemmArgs& a, f32x16 (&acc)[4
 // tid: the thread index. A caller may pass an opaque copy, so that the per-lane constants are
 // recomputed in every tile of a walk instead of computed once and, short of registers, spilled:
 // a reload waits for every load in flight, including DMAs issued for the next tile.
-template <uint32_t F, bool kSeeded = false>
+// kStage: bytes of `lds` a staged tile may use (a larger one goes in two passes of 128 tokens).
+template <uint32_t F, bool kSeeded = false, int kStage = accepi::kStageBytes>
 __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4][4], uint8_t* lds, const float* svec,
                                              int t0, int f0, int ft, int* slot, int tid) {
   using namespace accepi;
@@ -331,7 +332,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     const int es = dt_bytes(dt);
     const int cols = pr ? kTileCols / 2 : kTileCols;
     const int C = cols * es / 16;
-    const int passes = kTileRows * cols * es > kStageBytes ? 2 : 1;
+    const int passes = kTileRows * cols * es > kStage ? 2 : 1;
     const int R = kTileRows / passes;
 #pragma clang loop unroll(disable)
     for (int p = 0; p < passes; ++p) {
@@ -514,7 +515,7 @@ __device__ __forceinline__ void acc_epilogue(const GemmArgs& a, f32x16 (&acc)[4]
     const int zdt = cfg.z_dt();
     const int es = dt_bytes(zdt);
     const int C = kTileCols * es / 16;
-    const int passes = kTileRows * kTileCols * es > kStageBytes ? 2 : 1;
+    const int passes = kTileRows * kTileCols * es > kStage ? 2 : 1;
     const int R = kTileRows / passes;
 #pragma clang loop unroll(disable)
     for (int p = 0; p < passes; ++p) {

@@ -121,7 +121,8 @@ struct DmaPlan {
 // (a 64 KB staged tile, placed in stage 1) and the cross-entropy statistics (nothing staged
 // unless the logits are stored, which is checked at run time). In the tile walk they issue the
 // next tile's first DMAs (DmaPlan::head) as soon as the mainloop is done, so that data lands
-// while the epilogue runs instead of at the start of the next tile.
+// while the epilogue runs instead of at the start of the next tile. (A whole 16-bit tile would
+// need two 64 KB passes in stage 1; for MLP-up that cost more than the early DMAs saved.)
 template <uint32_t F>
 constexpr bool prefetches_head() {
   constexpr uint32_t kStages = epi::kZ | epi::kAux | epi::kPart | epi::kQuant | epi::kSplit | epi::kRope;
@@ -280,7 +281,7 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   }
   dma_x(1, 0);
   dma_w(1, 0); dma_w(1, 1); dma_x(1, 1);
-  if constexpr ((F & epi::kStatic) != 0 && !late_vectors<F>()) vp.store(svec);
+  if constexpr ((F & epi::kStatic) != 0 && !late_vectors<F>()) vp.store(svec, tid);
   if (head_loaded) dma_wait_barrier<12>();  // step 0, and every store before this tile
   else dma_wait_barrier<16>();              // X and W blocks 0-1 of step 0
   if constexpr (kBiasStart) {
@@ -346,7 +347,7 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int tt, int ft, uin
   constexpr bool kSeed = kDma && (accepi::seeds_residual<F>() || accepi::seeds_bias<F>());
   f32x16 acc[4][4];
   if constexpr (kDma && accepi::seeds_residual<F>()) {
-    if constexpr ((F & epi::kBias) != 0) vp.store(svec);  // seed_residual reads the bias
+    if constexpr ((F & epi::kBias) != 0) vp.store(svec, tid);  // seed_residual reads the bias
     accepi::seed_residual<F>(a, acc, smem, svec, t0, f0);
   } else if constexpr (kSeed) {
     // written in mainloop_dma
@@ -361,16 +362,16 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int tt, int ft, uin
   int tid_e = tid;  // the epilogue's thread index
   if constexpr (kDma) {
     mainloop_dma<F, kSeed && !accepi::seeds_residual<F>()>(a, smem, svec, vp, acc, t0, f0, head_loaded);
+    // An opaque copy of the thread index, taken before the next tile's DMAs: the epilogue's
+    // lane constants then come from it, and the thread index itself (held in scratch across the
+    // walk) is reloaded here, where nothing is in flight, not after the DMAs.
+    if constexpr (prefetches_head<F>()) asm volatile("" : "+v"(tid_e));
     if constexpr (late_vectors<F>()) {
       if constexpr (kLateLoad) vp.load<F>(a.ep, t0, f0, a.M, a.N);
-      vp.store(svec);  // nothing is in flight here
+      vp.store(svec, tid_e);  // nothing is in flight here
       lds_barrier();
     }
     if constexpr (prefetches_head<F>()) {
-      // An opaque copy of the thread index, taken before the DMAs: the epilogue's lane
-      // constants then come from it, and the thread index itself (held in scratch across the
-      // walk) is reloaded here, where nothing is in flight, not after the DMAs.
-      asm volatile("" : "+v"(tid_e));
       // the mainloop's last barrier has retired every read of both stages
       if (next_tt >= 0 && ((F & epi::kXent) == 0 || a.ep.y == nullptr)) {
         DmaPlan(a, smem, next_tt * BT, next_ft * BF, tid_e).head();
@@ -517,7 +518,7 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int tt, int ft, uin
     for (int q = 0; q < 4; ++q) store_q(0, q);
 #pragma unroll
     for (int q = 0; q < 4; ++q) load_q(BK, q);
-    if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
+    if constexpr ((F & epi::kStatic) != 0) vp.store(svec, tid);
     __syncthreads();
     read_frags(0, 0, fa[0], fb_[0]);
 
@@ -528,16 +529,18 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int tt, int ft, uin
 
   if constexpr ((F & epi::kStatic) != 0) {
     // Epilogue on the accumulators in place; the mainloop's LDS buffers (128 KB) stage
-    // the finished values for coalesced stores (stage 1 alone when the next head may be in stage 0).
-    // (The stage-1 offset is passed opaque: as a constant it would be folded into every LDS
-    // access and overflow their 16-bit offset fields, costing an address add per access.)
+    // the finished values for coalesced stores, or stage 1 alone (64 KB) when the next tile's
+    // head may be landing in stage 0. (The stage-1 offset is passed opaque: as a constant it
+    // would be folded into every LDS access and overflow their 16-bit offset fields, costing an
+    // address add per access.)
+    constexpr bool kStage1 = kDma && prefetches_head<F>() && (F & epi::kXent) == 0;
     uint8_t* lds = smem;
-    if constexpr (kDma && prefetches_head<F>() && (F & epi::kXent) == 0) {
+    if constexpr (kStage1) {
       int off = kBuf;
       asm volatile("" : "+s"(off));
       lds += off;
     }
-    acc_epilogue<F, kSeed>(a, acc, lds, svec, t0, f0, ft, slot, tid_e);
+    acc_epilogue<F, kSeed, kStage1 ? kBuf : 2 * kBuf>(a, acc, lds, svec, t0, f0, ft, slot, tid_e);
   } else {
     // Any other op list: the fp32 tile is staged through LDS in two 128-token passes
     // (128 KB each; pass p takes the accumulators of the waves with wt == p) and the

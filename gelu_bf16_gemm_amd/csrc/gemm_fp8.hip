@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_t256_kernel(GemmArgs a) 
   for (int q = 0; q < 4; ++q) store_q(0, q);
 #pragma unroll
   for (int q = 0; q < 4; ++q) load_q(BK, q);
-  if constexpr ((F & epi::kStatic) != 0) vp.store(svec);
+  if constexpr ((F & epi::kStatic) != 0) vp.store(svec, threadIdx.x);
   dqv[tid] = sw;
   dqv[256 + tid] = sa;
   __syncthreads();
