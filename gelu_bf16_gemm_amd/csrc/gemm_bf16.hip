@@ -188,11 +188,12 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   const DmaPlan d(a, smem, t0, f0, tid);
   const int wave = d.wave, lane = tid & 63;
   const int wf = wave >> 1, wt = wave & 1;
-  // With the next tile's head prefetched, the step count is opaque too: the loop's entry test
-  // would otherwise be hoisted out of the walk and held across every tile, and spilled, its
-  // reload waiting for the DMAs in flight. (The other instances measured more spills with it.)
+  // With the next tile's head prefetched, and with the residual seed, the step count is opaque
+  // too: the loop's entry test would otherwise be hoisted out of the walk and held across every
+  // tile, and spilled, its reload waiting for the DMAs in flight. (The other instances measured
+  // more spills with it.)
   int steps = a.K / BK;
-  if constexpr (prefetches_head<F>()) asm volatile("" : "+s"(steps));
+  if constexpr (prefetches_head<F>() || accepi::seeds_residual<F>()) asm volatile("" : "+s"(steps));
   // DMAs of steps past the last are still issued so that the wait counts stay exact.
   auto dma_w1 = [&](int t, int j, int g) __attribute__((always_inline)) { d.w1(t, j, g); };
   auto dma_x1 = [&](int t, int h, int g) __attribute__((always_inline)) { d.x1(t, h, g); };
@@ -273,6 +274,9 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   // head_loaded the previous tile's epilogue issued all of step 0 (DmaPlan::head) and the first
   // wait takes it whole, with the stores issued after it; from the next wait on, the DMAs in
   // flight are the same either way.
+  // the epilogue vectors go to LDS before the DMAs: their values are in registers by now, and
+  // a spilled one's reload after the DMAs would wait for all of them
+  if constexpr ((F & epi::kStatic) != 0 && !late_vectors<F>() && !accepi::seeds_residual<F>()) vp.store(svec, tid);
   head_loaded = prefetches_head<F>() && head_loaded;
   if (!head_loaded) {  // the same DMAs as DmaPlan::head
     dma_x(0, 0); dma_x(0, 1);
@@ -281,7 +285,6 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   }
   dma_x(1, 0);
   dma_w(1, 0); dma_w(1, 1); dma_x(1, 1);
-  if constexpr ((F & epi::kStatic) != 0 && !late_vectors<F>()) vp.store(svec, tid);
   if (head_loaded) dma_wait_barrier<12>();  // step 0, and every store before this tile
   else dma_wait_barrier<16>();              // X and W blocks 0-1 of step 0
   if constexpr (kBiasStart) {
@@ -347,7 +350,9 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int tt, int ft, uin
   constexpr bool kSeed = kDma && (accepi::seeds_residual<F>() || accepi::seeds_bias<F>());
   f32x16 acc[4][4];
   if constexpr (kDma && accepi::seeds_residual<F>()) {
-    if constexpr ((F & epi::kBias) != 0) vp.store(svec, tid);  // seed_residual reads the bias
+    // seed_residual reads the bias; the other vectors are stored here too, while nothing is
+    // in flight (after the prologue's DMAs a spilled vector value's reload would drain them)
+    vp.store(svec, tid);
     accepi::seed_residual<F>(a, acc, smem, svec, t0, f0);
   } else if constexpr (kSeed) {
     // written in mainloop_dma

@@ -28,7 +28,7 @@ CFG = {0: "generic", 2147833089: "bias+gelu_erf", 2147832961: "bias+split", 2147
        2148881537: "bias+split+rope"}
 # scratch bytes per lane allowed outside the K loop: (LDS-DMA mainloop, register-staged mainloop)
 T256_BUDGET = {"generic": (92, 0), "bias+gelu_erf": (0, 36), "bias+split": (0, 60),
-               "residual+aux+rms+gamma": (68, 136), "swiglu": (8, 52), "swiglu+fp8": (16, 32),
+               "residual+aux+rms+gamma": (64, 136), "swiglu": (8, 52), "swiglu+fp8": (16, 32),
                "rowscale+swiglu": (12, 36), "xent": (196, 252), "bias+split+rope": (52, 120)}
 # the other GEMM kernels, by instance (E4M3 inputs: epilogue configuration id; fp32: token tile)
 OTHER_BUDGET = {"gemm_fp8_t256_kernelILj2147833089E": 36, "gemm_fp8_t256_kernelILj2147832834E": 100,
