@@ -132,13 +132,20 @@ constexpr bool prefetches_head() {
   return ((F >> epi::kActShift) & 3) == ACT_SWIGLU && (y == FUSEDOPS_BF16 || y == FUSEDOPS_F16);
 }
 
-// Of those, the ones without a bias (which would start the accumulators in the mainloop):
-// only their epilogue reads the per-feature / per-token vectors, which are then stored to LDS
-// after the mainloop. Stored in the prologue, they would need the wait for their loads there,
-// which the compiler places after the prologue's DMAs, draining them.
+// Static configurations whose epilogue reads per-feature or per-token vectors (bias, column
+// or row scale, labels); the others fetch and store none.
+template <uint32_t F>
+constexpr bool has_vectors() {
+  return (F & epi::kStatic) != 0 && (F & (epi::kBias | epi::kGamma | epi::kRscale | epi::kXent)) != 0;
+}
+
+// Of the prefetching ones, those with vectors but no bias (which would start the accumulators
+// in the mainloop): only their epilogue reads the vectors, which are then stored to LDS after
+// the mainloop. Stored in the prologue, they would need the wait for their loads there, which
+// the compiler places after the prologue's DMAs, draining them.
 template <uint32_t F>
 constexpr bool late_vectors() {
-  return prefetches_head<F>() && (F & epi::kBias) == 0;
+  return prefetches_head<F>() && has_vectors<F>() && (F & epi::kBias) == 0;
 }
 
 // Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
@@ -276,7 +283,7 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& a, uint8_t* smem, f
   // flight are the same either way.
   // the epilogue vectors go to LDS before the DMAs: their values are in registers by now, and
   // a spilled one's reload after the DMAs would wait for all of them
-  if constexpr ((F & epi::kStatic) != 0 && !late_vectors<F>() && !accepi::seeds_residual<F>()) vp.store(svec, tid);
+  if constexpr (has_vectors<F>() && !late_vectors<F>() && !accepi::seeds_residual<F>()) vp.store(svec, tid);
   head_loaded = prefetches_head<F>() && head_loaded;
   if (!head_loaded) {  // the same DMAs as DmaPlan::head
     dma_x(0, 0); dma_x(0, 1);
@@ -341,7 +348,7 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int tt, int ft, uin
   // its loads at once, and the waits for them would delay the prologue's DMAs)
   constexpr bool kLateLoad = kDma && late_vectors<F>() && (F & epi::kRscale) != 0;
   accepi::VecPrefetch vp;
-  if constexpr ((F & epi::kStatic) != 0 && !kLateLoad) vp.load<F>(a.ep, t0, f0, a.M, a.N);
+  if constexpr (has_vectors<F>() && !kLateLoad) vp.load<F>(a.ep, t0, f0, a.M, a.N);
 
   // On the LDS-DMA path a static configuration's accumulators start from its residual and
   // bias (seed_residual) or, without a residual, from its bias (in mainloop_dma): the MFMAs
@@ -352,7 +359,7 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int tt, int ft, uin
   if constexpr (kDma && accepi::seeds_residual<F>()) {
     // seed_residual reads the bias; the other vectors are stored here too, while nothing is
     // in flight (after the prologue's DMAs a spilled vector value's reload would drain them)
-    vp.store(svec, tid);
+    if constexpr (has_vectors<F>()) vp.store(svec, tid);
     accepi::seed_residual<F>(a, acc, smem, svec, t0, f0);
   } else if constexpr (kSeed) {
     // written in mainloop_dma
@@ -523,7 +530,7 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, int tt, int ft, uin
     for (int q = 0; q < 4; ++q) store_q(0, q);
 #pragma unroll
     for (int q = 0; q < 4; ++q) load_q(BK, q);
-    if constexpr ((F & epi::kStatic) != 0) vp.store(svec, tid);
+    if constexpr (has_vectors<F>()) vp.store(svec, tid);
     __syncthreads();
     read_frags(0, 0, fa[0], fb_[0]);
 
